@@ -1,0 +1,208 @@
+"""Host-side checks of the C ABI (CPU only: nothing here launches a kernel).
+
+The library must load, export every function include/sp_region.h declares, and
+reject bad arguments synchronously with the documented status codes.  Every
+call below fails validation (or is an empty shard) before any HIP call, so the
+fake device addresses are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import transformer_sequence_activation_amd as sp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sp_region.h")
+
+A = 0x7F0000000000  # a 16-byte aligned fake device address range base
+
+
+def fake(i, misalign=0):
+    return A + i * (1 << 32) + misalign
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sp_region_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return sp.load()
+
+
+def test_library_exports_every_declared_function(lib):
+    names = header_functions()
+    assert set(names) == set(sp.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sp.sp_region_version() >= 100
+
+
+def test_strerror_covers_every_status(lib):
+    for code in sp.STATUS:
+        assert sp.sp_region_strerror(code)
+    assert "unknown" in sp.sp_region_strerror(12345)
+
+
+def good_desc(**kw):
+    base = dict(S=64, B=2, H=256, T=4, j=1, dtype="bf16", norm="rms", eps=1e-6, p=0.1, seed=1)
+    base.update(kw)
+    return sp.make_desc(**base)
+
+
+def fwd_call(desc, P=None, residual=None, gamma=None, beta=None, h=None, y=None, mask=None,
+             mean=None, rstd=None):
+    T = desc.T
+    P = [fake(10 + t) for t in range(T)] if P is None else P
+    ln = desc.norm == sp.SP_LAYERNORM
+    return sp.sp_region_fwd(
+        desc, P,
+        fake(1) if residual is None else residual,
+        fake(2) if gamma is None else gamma,
+        (fake(3) if ln else None) if beta is None else beta,
+        fake(4) if h is None else h,
+        fake(5) if y is None else y,
+        fake(6) if mask is None else mask,
+        (fake(7) if ln else None) if mean is None else mean,
+        fake(8) if rstd is None else rstd,
+        stream=0)
+
+
+def bwd_call(desc, ws_bytes=None, **over):
+    ln = desc.norm == sp.SP_LAYERNORM
+    args = dict(dY=fake(1), h=fake(2), mask=fake(3), mean=fake(4) if ln else None, rstd=fake(5),
+                gamma=fake(6), dR=None, d_residual=fake(7), dP=fake(8), dgamma=fake(9),
+                dbeta=fake(10) if ln else None, workspace=fake(11))
+    args.update(over)
+    if ws_bytes is None:
+        ws_bytes = sp.sp_region_bwd_workspace_size(desc)
+    return sp.sp_region_bwd(desc, args["dY"], args["h"], args["mask"], args["mean"], args["rstd"],
+                            args["gamma"], args["dR"], args["d_residual"], args["dP"],
+                            args["dgamma"], args["dbeta"], args["workspace"], ws_bytes, stream=0)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), -3),
+    (dict(norm=5), -4),
+    (dict(p=1.0), -4), (dict(p=-0.1), -4), (dict(p=float("nan")), -4),
+    (dict(eps=-1.0), -4), (dict(eps=float("inf")), -4),
+    (dict(H=0), -2), (dict(H=-8), -2), (dict(S=-2), -2), (dict(B=-1), -2),
+    (dict(T=0, j=0), -2), (dict(T=65, j=0, S=65 * 2), -2),
+    (dict(j=4), -2), (dict(j=-1), -2),
+    (dict(S=66), -2),                       # S % T != 0
+    (dict(H=100), -2),                      # bf16 row not a multiple of 16 bytes
+    (dict(H=6, dtype="f32"), -2),           # fp32 row not a multiple of 16 bytes
+    (dict(H=65536 + 8), -2),                # row above SP_MAX_H_BYTES
+])
+def test_descriptor_errors(lib, kw, code):
+    d = good_desc(**kw)
+    assert fwd_call(d) == code
+    assert bwd_call(d, ws_bytes=1 << 30) == code
+    f, b = ctypes.c_uint64(), ctypes.c_uint64()
+    assert lib.sp_region_traffic_bytes(ctypes.byref(d), ctypes.byref(f), ctypes.byref(b)) == code
+    assert sp.sp_region_bwd_workspace_size(d) == 0
+
+
+def test_null_descriptor(lib):
+    assert lib.sp_region_fwd(None, None, None, None, None, None, None, None, None, None, None) == -1
+    assert lib.sp_region_bwd_workspace_size(None) == 0
+
+
+@pytest.mark.parametrize("over", [
+    dict(residual=0), dict(gamma=0), dict(h=0), dict(y=0), dict(mask=0), dict(rstd=0),
+    dict(P=[fake(10), 0, fake(12), fake(13)]),
+])
+def test_fwd_null_pointers(lib, over):
+    over = {k: (None if v == 0 else v) for k, v in over.items()}
+    if "P" in over:
+        over["P"] = [x if x else None for x in over["P"]]
+    d = good_desc()
+    # a None that reaches C as NULL must be rejected
+    T = d.T
+    P = over.get("P", [fake(10 + t) for t in range(T)])
+    args = dict(residual=fake(1), gamma=fake(2), h=fake(4), y=fake(5), mask=fake(6), rstd=fake(8))
+    args.update({k: v for k, v in over.items() if k != "P"})
+    rc = sp.sp_region_fwd(d, P, args["residual"], args["gamma"], None, args["h"], args["y"],
+                          args["mask"], None, args["rstd"], stream=0)
+    assert rc == -1
+
+
+def test_fwd_norm_specific_pointers(lib):
+    rms, ln = good_desc(norm="rms"), good_desc(norm="ln")
+    assert fwd_call(rms, beta=fake(3)) == -1           # beta given to RMSNorm
+    assert fwd_call(rms, mean=fake(7)) == -1           # mean output for RMSNorm
+    assert sp.sp_region_fwd(ln, [fake(10 + t) for t in range(4)], fake(1), fake(2), None, fake(4),
+                            fake(5), fake(6), fake(7), fake(8), stream=0) == -1  # LN without beta
+    assert sp.sp_region_fwd(ln, [fake(10 + t) for t in range(4)], fake(1), fake(2), fake(3),
+                            fake(4), fake(5), fake(6), None, fake(8), stream=0) == -1  # LN without mean
+
+
+@pytest.mark.parametrize("which", ["residual", "gamma", "h", "y", "mask", "rstd", "P"])
+def test_fwd_misaligned(lib, which):
+    d = good_desc()
+    if which == "P":
+        assert fwd_call(d, P=[fake(10), fake(11, 2), fake(12), fake(13)]) == -5
+    else:
+        assert fwd_call(d, **{which: fake(20, 8)}) == -5
+
+
+def test_fwd_overlapping_outputs(lib):
+    d = good_desc()
+    R, H = d.R, d.H
+    assert fwd_call(d, y=fake(4) + 16) == -1                    # y inside h
+    assert fwd_call(d, h=fake(1)) == -1                         # h aliases the residual
+    base = d.j * R * H * 2
+    assert fwd_call(d, mask=fake(11) + base) == -1              # mask inside P_1's shard slab
+
+
+def test_fwd_empty_shard_is_a_noop(lib):
+    for S in (0,):
+        assert fwd_call(good_desc(S=S)) == 0
+    assert fwd_call(good_desc(B=0)) == 0
+
+
+def test_bwd_errors(lib):
+    d = good_desc()
+    need = sp.sp_region_bwd_workspace_size(d)
+    assert need > 0
+    assert bwd_call(d, ws_bytes=need - 1) == -6
+    assert bwd_call(d, workspace=None) == -6
+    assert bwd_call(d, workspace=fake(11, 4)) == -5
+    assert bwd_call(d, dY=None) == -1
+    assert bwd_call(d, dbeta=fake(10)) == -1                   # dbeta for RMSNorm
+    assert bwd_call(good_desc(norm="ln"), mean=None) == -1
+    assert bwd_call(d, dR=fake(12, 2)) == -5
+    assert bwd_call(d, dP=fake(7) + 32) == -1                  # dP overlaps d_residual
+    assert bwd_call(d, workspace=fake(9)) == -1                # workspace overlaps dgamma
+    assert bwd_call(d, d_residual=fake(2)) == -1               # writes over h
+
+
+def test_traffic_bytes_follow_the_accounting(lib):
+    # the pages' F: one full-sequence bf16 [S,B,H] tensor at B=2, S=2048, H=768 is 6 MiB
+    F = 6 * 1024 * 1024
+    d = sp.make_desc(2048, 2, 768, 1, 0, "bf16", "rms")
+    fwd, bwd = sp.sp_region_traffic_bytes(d)
+    R, H = 2048 * 2, 768
+    # T=1: one partial + residual + h + y (4 F) + mask (F/2) + rstd + gamma
+    assert fwd == 4 * F + F // 2 + 4 * R + 4 * H
+    # dY + h + d_residual + dP (4 F) + mask + rstd + gamma + dgamma
+    assert bwd == 4 * F + F // 2 + 4 * R + 4 * H + 4 * H
+    # per element, bf16: (2T + 7) bytes forward and 9 bytes backward, plus per-row/col terms
+    for T, norm in ((2, "rms"), (8, "ln")):
+        d = sp.make_desc(4096, 1, 4096, T, 3 % T, "bf16", norm)
+        fwd, bwd = sp.sp_region_traffic_bytes(d)
+        N, R = d.R * 4096, d.R
+        k = 2 if norm == "ln" else 1
+        assert fwd == (2 * T + 7) * N + 4 * R * k + 4 * 4096 * k
+        assert bwd == 9 * N + 4 * R * k + 4 * 4096 + 4 * 4096 * k
+
+
+def test_workspace_size_scales_with_norm(lib):
+    rms = sp.sp_region_bwd_workspace_size(good_desc(norm="rms"))
+    ln = sp.sp_region_bwd_workspace_size(good_desc(norm="ln"))
+    assert ln == 2 * rms and rms % 16 == 0
+    assert sp.sp_region_bwd_workspace_size(good_desc(S=0)) == 0

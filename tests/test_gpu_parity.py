@@ -1,0 +1,391 @@
+"""Parity of the HIP path with the CPU oracle, through the C ABI (GPU).
+
+Bar: the dropout mask byte-identical; h bit-identical where expected (both
+sides add in fp32 in the same order and round once); every float output within
+|got - ref| <= rtol*|ref| + rtol*rms(ref), rtol = 1e-2 for bf16 outputs and
+for dgamma/dbeta, 1e-5 for fp32 outputs and for the fp32 statistics (the
+scale of mean is |mean| + 1/rstd).
+
+Small workloads are compared element by element over whole shards; the two
+large ones over whole shards where the oracle finishes in seconds and over
+sampled token rows (including outlier rows) otherwise, plus properties that
+hold at any size.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import transformer_sequence_activation_amd as sp
+from transformer_sequence_activation_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+RTOL_BF16 = 1e-2
+RTOL_F32 = 1e-5
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu(hip_lib):
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+
+
+# ---------------------------------------------------------------------------
+# helpers
+
+def to_np(t):
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def as_f64(a, dtype):
+    if dtype == "bf16":
+        return oracle.bf16_to_f32(a).astype(np.float64)
+    return np.asarray(a, np.float64)
+
+
+def close(got, ref, rtol, what, scale=None):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    if ref.size == 0:
+        return
+    rms = math.sqrt(float(np.mean(ref ** 2)))
+    bound = rtol * (np.abs(ref) if scale is None else scale) + rtol * rms
+    err = np.abs(got - ref)
+    bad = ~(err <= bound)
+    assert not bad.any(), (f"{what}: {int(bad.sum())} of {ref.size} outside tolerance; "
+                           f"worst err {err.max():.3e} at {np.unravel_index(np.argmax(err - bound), err.shape)}")
+
+
+def odesc(w, j, dtype=None):
+    dt = {"bf16": oracle.BF16, "f32": oracle.F32}[dtype or w.dtype]
+    nm = oracle.LAYERNORM if w.norm == "ln" else oracle.RMSNORM
+    return oracle.make_desc(w.S, w.B, w.H, w.T, j, dt, nm, w.eps, w.p, w.seed)
+
+
+def gdesc(w, j):
+    return sp.make_desc(w.S, w.B, w.H, w.T, j, w.dtype, w.norm, w.eps, w.p, w.seed)
+
+
+class Case:
+    """Inputs of one workload: full tensors on the GPU, CPU copies on demand."""
+
+    def __init__(self, w, gen_device):
+        self.w = w
+        self.P = [W.partial(w, t, gen_device).to("cuda") for t in range(w.T)]
+        self.res = W.residual(w, gen_device).to("cuda")
+        self.dY = W.grad_y(w, gen_device).to("cuda")
+        self.gamma = W.gamma(w, gen_device).to("cuda")
+        b = W.beta(w, gen_device)
+        self.beta = None if b is None else b.to("cuda")
+
+    def shard(self, full, j):
+        return W.shard(full, self.w, j)
+
+    def host_rows(self, full, j, rows=None):
+        s = self.shard(full, j)
+        if rows is not None:
+            s = s[rows]
+        return to_np(s)
+
+
+def gpu_fwd(c, j):
+    d = gdesc(c.w, j)
+    return sp.forward(d, c.P, c.shard(c.res, j), c.gamma, c.beta)
+
+
+def gpu_bwd(c, j, f, dR=None):
+    d = gdesc(c.w, j)
+    return sp.backward(d, c.shard(c.dY, j), f["h"], f["mask"], f["mean"], f["rstd"], c.gamma, dR=dR)
+
+
+def oracle_fwd(c, j, row0=0, nrows=None):
+    w = c.w
+    nrows = w.R - row0 if nrows is None else nrows
+    sl = slice(row0, row0 + nrows)
+    P = [c.host_rows(p, j, sl) for p in c.P]
+    res = c.host_rows(c.res, j, sl)
+    gam = to_np(c.gamma).astype(np.float64)
+    bet = None if c.beta is None else to_np(c.beta).astype(np.float64)
+    return oracle.fwd(odesc(w, j), P, res, gam, bet, row0=row0, nrows=nrows)
+
+
+def oracle_bwd(c, j, of, row0=0, nrows=None, dR=None):
+    w = c.w
+    nrows = w.R - row0 if nrows is None else nrows
+    sl = slice(row0, row0 + nrows)
+    dY = c.host_rows(c.dY, j, sl)
+    gam = to_np(c.gamma).astype(np.float64)
+    # the stored statistics are fp32 on both sides
+    mean = None if of["mean"] is None else of["mean"].astype(np.float32).astype(np.float64)
+    rstd = of["rstd"].astype(np.float32).astype(np.float64)
+    return oracle.bwd(odesc(w, j), dY, of["h"], of["mask"], mean, rstd, gam, dR=dR, row0=row0,
+                      nrows=nrows)
+
+
+def compare_fwd(w, g, o, rows=None, h_exact=True):
+    gh, gy, gm = to_np(g["h"]), to_np(g["y"]), to_np(g["mask"])
+    grs = to_np(g["rstd"])
+    gmu = None if g["mean"] is None else to_np(g["mean"])
+    if rows is not None:
+        gh, gy, gm, grs = gh[rows], gy[rows], gm[rows], grs[rows]
+        gmu = None if gmu is None else gmu[rows]
+    assert np.array_equal(gm, o["mask"]), "mask differs"
+    if h_exact:
+        assert np.array_equal(gh, o["h"]), f"h not bit-identical ({int((gh != o['h']).sum())} elements)"
+    rt = RTOL_BF16 if w.dtype == "bf16" else RTOL_F32
+    close(as_f64(gh, w.dtype), as_f64(o["h"], w.dtype), rt, "h")
+    close(as_f64(gy, w.dtype), as_f64(o["y"], w.dtype), rt, "y")
+    close(grs, o["rstd"], RTOL_F32, "rstd", scale=np.abs(o["rstd"]))
+    if gmu is not None:
+        close(gmu, o["mean"], RTOL_F32, "mean", scale=np.abs(o["mean"]) + 1 / o["rstd"])
+
+
+def compare_bwd(w, g, o, rows=None, with_dgamma=True):
+    gr, gp = to_np(g["d_res"]), to_np(g["dP"])
+    if rows is not None:
+        gr, gp = gr[rows], gp[rows]
+    rt = RTOL_BF16 if w.dtype == "bf16" else RTOL_F32
+    close(as_f64(gr, w.dtype), as_f64(o["d_res"], w.dtype), rt, "d_residual")
+    close(as_f64(gp, w.dtype), as_f64(o["dP"], w.dtype), rt, "dP")
+    if with_dgamma:
+        close(to_np(g["dgamma"]), o["dgamma"], RTOL_BF16, "dgamma")
+        if o["dbeta"] is not None:
+            close(to_np(g["dbeta"]), o["dbeta"], RTOL_BF16, "dbeta")
+
+
+# ---------------------------------------------------------------------------
+# the workloads
+
+SMALL = [("tiny_fp32_T2_S256_B1_H64", 0), ("minimind_T2_S2048_B2_H768", 0),
+         ("minimind_T2_S2048_B2_H768", 1), ("layernorm_T8_S4096_B1_H4096", 3)]
+
+
+@pytest.fixture(scope="module")
+def small_cases():
+    return {}
+
+
+@pytest.mark.parametrize("name,j", SMALL)
+def test_workload_matches_oracle_whole_shard(small_cases, name, j):
+    w = W.WORKLOADS[name]
+    print(f"\n[case] {name} shard {j}: forward, backward vs oracle", flush=True)
+    if name not in small_cases:
+        small_cases[name] = Case(w, "cpu")
+    c = small_cases[name]
+    g = gpu_fwd(c, j)
+    torch.cuda.synchronize()
+    o = oracle_fwd(c, j)
+    compare_fwd(w, g, o)
+    if w.fwd_only:
+        return
+    gb = gpu_bwd(c, j, g)
+    torch.cuda.synchronize()
+    ob = oracle_bwd(c, j, o)
+    compare_bwd(w, gb, ob)
+
+
+def test_backward_on_oracle_saved_tensors():
+    """The backward alone: both sides read the same saved h, mask and fp32 stats."""
+    w = W.WORKLOADS["minimind_T2_S2048_B2_H768"]
+    print("\n[case] minimind shard 1: backward on the oracle's saved tensors", flush=True)
+    c = Case(w, "cpu")
+    j = 1
+    o = oracle_fwd(c, j)
+    d = gdesc(w, j)
+    h = torch.from_numpy(o["h"].view(np.int16)).view(torch.bfloat16).cuda()
+    mask = torch.from_numpy(o["mask"]).cuda()
+    rstd = torch.from_numpy(o["rstd"].astype(np.float32)).cuda()
+    gb = sp.backward(d, c.shard(c.dY, j), h, mask, None, rstd, c.gamma)
+    torch.cuda.synchronize()
+    compare_bwd(w, gb, oracle_bwd(c, j, o))
+
+
+def test_large_hidden_whole_shard():
+    w = W.WORKLOADS["large_hidden_T8_S8192_B2_H8192"]
+    j = w.shards[0]
+    print(f"\n[case] {w.name} shard {j}: full-size forward, backward vs oracle", flush=True)
+    c = Case(w, "cuda")
+    g = gpu_fwd(c, j)
+    gb = gpu_bwd(c, j, g)
+    torch.cuda.synchronize()
+    o = oracle_fwd(c, j)
+    compare_fwd(w, g, o)
+    compare_bwd(w, gb, oracle_bwd(c, j, o))
+
+
+def test_long_sequence_all_shards():
+    """All eight shards at full size: sampled rows (outliers included) against
+    the oracle, the whole of shard 0 including dgamma, and properties of every
+    shard that hold at any size."""
+    w = W.WORKLOADS["long_seq_T8_S32768_B1_H8192"]
+    c = Case(w, "cuda")
+    outl = W.outlier_rows(w, "cuda").cpu().numpy()
+    rng = np.random.default_rng(5)
+    keep_total = 0
+    for j in w.shards:
+        print(f"\n[case] {w.name} shard {j}: full-size forward, backward", flush=True)
+        g = gpu_fwd(c, j)
+        gb = gpu_bwd(c, j, g)
+        torch.cuda.synchronize()
+        in_shard = outl[(outl >= j * w.R) & (outl < (j + 1) * w.R)] - j * w.R
+        rows = np.unique(np.concatenate([[0, w.R - 1], rng.choice(w.R, 12, replace=False),
+                                         in_shard[:6]])).astype(np.int64)
+        for r in rows:
+            o = oracle_fwd(c, j, row0=int(r), nrows=1)
+            compare_fwd(w, g, o, rows=[int(r)])
+            ob = oracle_bwd(c, j, o, row0=int(r), nrows=1)
+            compare_bwd(w, gb, ob, rows=[int(r)], with_dgamma=False)
+        if j == 0:
+            o = oracle_fwd(c, j)
+            compare_fwd(w, g, o)
+            compare_bwd(w, gb, oracle_bwd(c, j, o))
+        # properties at full size: unit RMS of y/gamma per row (up to eps and
+        # bf16 rounding), binomial keep count, dropped elements get no dP
+        y = g["y"].float() / c.gamma.float()
+        rms = torch.sqrt((y * y).mean(dim=1))
+        assert torch.all((rms - 1).abs() < 2e-2), float((rms - 1).abs().max())
+        keep = int(g["mask"].sum(dtype=torch.int64))
+        keep_total += keep
+        N = w.N
+        assert abs(keep - N * (1 - w.p)) <= 5 * math.sqrt(N * w.p * (1 - w.p))
+        assert int((gb["dP"][g["mask"] == 0] != 0).sum()) == 0
+        del g, gb
+    Nt = w.N * w.T
+    assert abs(keep_total - Nt * (1 - w.p)) <= 5 * math.sqrt(Nt * w.p * (1 - w.p))
+
+
+def test_runs_are_bitwise_identical():
+    w = W.WORKLOADS["layernorm_T8_S4096_B1_H4096"]
+    print(f"\n[case] {w.name}: two runs bitwise", flush=True)
+    c = Case(w, "cuda")
+    a = gpu_fwd(c, 3)
+    ab = gpu_bwd(c, 3, a)
+    b = gpu_fwd(c, 3)
+    bb = gpu_bwd(c, 3, b)
+    torch.cuda.synchronize()
+    for k in ("h", "y", "mask", "mean", "rstd"):
+        assert torch.equal(a[k], b[k]), k
+    for k in ("d_res", "dP", "dgamma", "dbeta"):
+        assert torch.equal(ab[k], bb[k]), k
+
+
+# ---------------------------------------------------------------------------
+# edge cases: ragged rows and columns, odd and extreme T, p at its ends,
+# smallest and largest rows, fp32 with LayerNorm, the residual-gradient input
+
+EDGE = [
+    # T, S, B, H, dtype, norm, p, j
+    (3, 21, 1, 776, "bf16", "rms", 0.1, 2),     # odd T, ragged chunks, ragged row tiles
+    (5, 35, 3, 1032, "bf16", "ln", 0.3, 4),     # T with no fixed-T kernel
+    (1, 17, 2, 4096, "bf16", "ln", 0.1, 0),     # T = 1
+    (64, 128, 1, 256, "bf16", "rms", 0.1, 63),  # T = SP_MAX_T
+    (2, 64, 3, 8, "bf16", "rms", 0.5, 1),       # one chunk per row
+    (4, 64, 2, 4, "f32", "ln", 0.2, 3),         # fp32, one chunk per row
+    (2, 40, 5, 2000, "f32", "ln", 0.1, 1),      # fp32 LayerNorm, ragged
+    (8, 64, 1, 8192, "bf16", "rms", 0.0, 7),    # p = 0 keeps everything
+    (8, 16, 1, 4096, "bf16", "ln", 0.9, 2),     # p near 1
+    (2, 6, 1, 65536, "bf16", "rms", 0.1, 1),    # the longest bf16 row
+    (2, 4, 1, 32768, "f32", "ln", 0.1, 0),      # the longest fp32 row
+    (4, 4096, 4, 128, "bf16", "ln", 0.1, 2),    # many short rows
+]
+
+
+def _edge_case(T, S, B, H, dtype, norm, p, j, seed=99):
+    w = W.Workload(f"edge_T{T}_S{S}_B{B}_H{H}", 900 + T, T, S, B, H, dtype, norm,
+                   1e-5 if norm == "ln" else 1e-6, p, (j,), seed=seed)
+    return Case(w, "cpu")
+
+
+@pytest.mark.parametrize("T,S,B,H,dtype,norm,p,j", EDGE)
+def test_edge_shapes_match_oracle(T, S, B, H, dtype, norm, p, j):
+    print(f"\n[case] edge T={T} S={S} B={B} H={H} {dtype} {norm} p={p} j={j}", flush=True)
+    c = _edge_case(T, S, B, H, dtype, norm, p, j)
+    g = gpu_fwd(c, j)
+    gb = gpu_bwd(c, j, g)
+    torch.cuda.synchronize()
+    o = oracle_fwd(c, j)
+    compare_fwd(c.w, g, o)
+    compare_bwd(c.w, gb, oracle_bwd(c, j, o))
+    if p == 0.0:
+        assert bool(g["mask"].all())
+
+
+@pytest.mark.parametrize("norm", ["rms", "ln"])
+def test_residual_gradient_input(norm):
+    print(f"\n[case] dR input, {norm}", flush=True)
+    c = _edge_case(4, 64, 2, 1024, "bf16", norm, 0.2, 1)
+    j = 1
+    dR_full = W._randn((c.w.S, c.w.B, c.w.H), 1.0, "cpu", 4242).to(torch.bfloat16)
+    dR = c.shard(dR_full, j).cuda()
+    g = gpu_fwd(c, j)
+    gb = gpu_bwd(c, j, g, dR=dR)
+    torch.cuda.synchronize()
+    o = oracle_fwd(c, j)
+    compare_bwd(c.w, gb, oracle_bwd(c, j, o, dR=to_np(dR)))
+
+
+def test_rounding_ties_to_even():
+    """Partial sums that fall exactly halfway between two bf16 values round to
+    the even one, as the oracle does."""
+    print("\n[case] bf16 rounding ties", flush=True)
+    H, S, T = 64, 2, 2
+    # 1 + 2^-8 -> 1 (even), 1 + 3*2^-8 -> 1 + 2^-6 (even), and the same at -2
+    base = torch.tensor([1.0, 1.0, -2.0, -2.0], dtype=torch.float32).repeat(H // 4)
+    off = torch.tensor([2.0 ** -8, 3 * 2.0 ** -8, -(2.0 ** -7), -3 * 2.0 ** -7]).repeat(H // 4)
+    P0 = base.view(1, 1, H).repeat(S, 1, 1)
+    P1 = off.view(1, 1, H).repeat(S, 1, 1)
+    P = [P0.to(torch.bfloat16).cuda(), P1.to(torch.bfloat16).cuda()]
+    res = torch.zeros(1, H, dtype=torch.bfloat16, device="cuda")
+    gam = torch.ones(H, device="cuda")
+    d = sp.make_desc(S, 1, H, T, 0, "bf16", "rms", 1e-6, 0.0, 1)
+    g = sp.forward(d, P, res, gam)
+    torch.cuda.synchronize()
+    od = oracle.make_desc(S, 1, H, T, 0, oracle.BF16, oracle.RMSNORM, 1e-6, 0.0, 1)
+    o = oracle.fwd(od, [to_np(p.view(S, H)[:1]) for p in P], to_np(res), np.ones(H))
+    assert np.array_equal(to_np(g["h"]), o["h"])
+    # the ties really are ties: exact sums have 0x8000 in the dropped half
+    exact = (P0 + P1).view(S, H)[0].numpy().view(np.uint32)
+    assert np.all((exact & 0xFFFF) == 0x8000)
+
+
+def test_empty_shard():
+    print("\n[case] empty shard", flush=True)
+    d = sp.make_desc(0, 2, 256, 2, 1, "bf16", "ln", 1e-5, 0.1, 1)
+    P = [torch.empty(0, 2, 256, dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    z = torch.empty(0, 256, dtype=torch.bfloat16, device="cuda")
+    gam = torch.ones(256, device="cuda")
+    bet = torch.zeros(256, device="cuda")
+    f = sp.forward(d, P, z, gam, bet)
+    dg = torch.full((256,), 7.0, device="cuda")
+    db = torch.full((256,), 7.0, device="cuda")
+    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    rc = sp.sp_region_bwd(d, z, f["h"], f["mask"], f["mean"], f["rstd"], gam, None,
+                          torch.empty_like(z), torch.empty_like(z), dg, db, ws, 16)
+    torch.cuda.synchronize()
+    assert rc == 0
+    assert bool((dg == 0).all()) and bool((db == 0).all())
+
+
+def test_gpu_argument_errors_leave_outputs_untouched():
+    print("\n[case] argument errors on real tensors", flush=True)
+    d = sp.make_desc(16, 1, 256, 2, 0, "bf16", "rms", 1e-6, 0.1, 1)
+    P = [torch.randn(16, 1, 256, device="cuda").to(torch.bfloat16) for _ in range(2)]
+    res = torch.randn(8, 256, device="cuda").to(torch.bfloat16)
+    gam = torch.ones(256, device="cuda")
+    h = torch.full((8, 256), 3.0, dtype=torch.bfloat16, device="cuda")
+    y = torch.full((8, 256), 3.0, dtype=torch.bfloat16, device="cuda")
+    m = torch.full((8, 256), 3, dtype=torch.uint8, device="cuda")
+    rs = torch.full((8,), 3.0, device="cuda")
+    raw = torch.empty(8 * 256 * 2 + 16, dtype=torch.uint8, device="cuda")
+    mis = raw.data_ptr() + 2  # 2-byte misaligned view of real memory
+    assert sp.sp_region_fwd(d, P, mis, gam, None, h, y, m, None, rs) == -5
+    assert sp.sp_region_fwd(d, P, res, gam, None, h, h, m, None, rs) == -1
+    torch.cuda.synchronize()
+    assert bool((h == 3).all()) and bool((y == 3).all()) and bool((m == 3).all())

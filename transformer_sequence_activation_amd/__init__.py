@@ -1,0 +1,231 @@
+"""Python binding of libsp_region.so, the MI355X sequence-parallel region kernels.
+
+Argument marshalling only: every step of the forward and backward runs in the
+HIP kernels of csrc/sp_region.hip.  PyTorch supplies device memory and the
+stream.  The C entry points are exposed under their C names
+(`sp_region_fwd`, `sp_region_bwd`, `sp_region_bwd_workspace_size`,
+`sp_region_traffic_bytes`, `sp_region_strerror`, `sp_region_version`); `forward`
+and `backward` allocate the outputs with torch and call them.
+
+If the shared library is missing, `load()` raises: there is no fallback path.
+"""
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libsp_region.so")
+
+SP_MAX_T = 64
+SP_F32, SP_BF16 = 0, 1
+SP_RMSNORM, SP_LAYERNORM = 0, 1
+SP_OK = 0
+STATUS = {0: "SP_OK", -1: "SP_EINVAL", -2: "SP_ESHAPE", -3: "SP_EDTYPE", -4: "SP_EPARAM",
+          -5: "SP_EALIGN", -6: "SP_EWORKSPACE", -7: "SP_EHIP"}
+EXPORTED = ("sp_region_fwd", "sp_region_bwd", "sp_region_bwd_workspace_size",
+            "sp_region_traffic_bytes", "sp_region_strerror", "sp_region_version")
+
+
+class SpDesc(ctypes.Structure):
+    """sp_desc_t of include/sp_region.h."""
+    _fields_ = [
+        ("S", ctypes.c_int64), ("B", ctypes.c_int64), ("H", ctypes.c_int64),
+        ("T", ctypes.c_int32), ("j", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("norm", ctypes.c_int32),
+        ("eps", ctypes.c_float), ("p", ctypes.c_float),
+        ("seed", ctypes.c_uint64),
+    ]
+
+    @property
+    def R(self):
+        return (self.S // self.T) * self.B if self.T > 0 else 0
+
+
+class SpRegionError(RuntimeError):
+    def __init__(self, status, text):
+        super().__init__(f"{STATUS.get(status, status)}: {text}")
+        self.status = status
+
+
+_lib = None
+
+
+def load(path=LIB_PATH):
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m transformer_sequence_activation_amd.build`")
+    L = ctypes.CDLL(path)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    pdesc = ctypes.POINTER(SpDesc)
+    L.sp_region_fwd.argtypes = [pdesc, ctypes.POINTER(vp), vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.sp_region_fwd.restype = ctypes.c_int
+    L.sp_region_bwd.argtypes = [pdesc, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.sp_region_bwd.restype = ctypes.c_int
+    L.sp_region_bwd_workspace_size.argtypes = [pdesc]
+    L.sp_region_bwd_workspace_size.restype = sz
+    L.sp_region_traffic_bytes.argtypes = [pdesc, ctypes.POINTER(ctypes.c_uint64),
+                                          ctypes.POINTER(ctypes.c_uint64)]
+    L.sp_region_traffic_bytes.restype = ctypes.c_int
+    L.sp_region_strerror.argtypes = [ctypes.c_int]
+    L.sp_region_strerror.restype = ctypes.c_char_p
+    L.sp_region_version.argtypes = []
+    L.sp_region_version.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def make_desc(S, B, H, T, j, dtype="bf16", norm="rms", eps=1e-6, p=0.1, seed=1234):
+    dt = {"bf16": SP_BF16, "f32": SP_F32}.get(dtype, dtype)
+    nm = {"rms": SP_RMSNORM, "ln": SP_LAYERNORM}.get(norm, norm)
+    return SpDesc(S, B, H, T, j, dt, nm, eps, p, seed)
+
+
+def _ptr(x):
+    """Device address of a tensor (or an int address / None)."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status):
+    if status != SP_OK:
+        raise SpRegionError(status, sp_region_strerror(status))
+
+
+# ---- the C entry points, same names, tensors or raw addresses in ----
+
+def sp_region_version():
+    return load().sp_region_version()
+
+
+def sp_region_strerror(status):
+    return load().sp_region_strerror(status).decode()
+
+
+def sp_region_traffic_bytes(desc):
+    f, b = ctypes.c_uint64(), ctypes.c_uint64()
+    _check(load().sp_region_traffic_bytes(ctypes.byref(desc), ctypes.byref(f), ctypes.byref(b)))
+    return f.value, b.value
+
+
+def sp_region_bwd_workspace_size(desc):
+    return load().sp_region_bwd_workspace_size(ctypes.byref(desc))
+
+
+def sp_region_fwd(desc, P, residual, gamma, beta, h_out, y_out, mask_out, mean_out, rstd_out,
+                  stream=None):
+    """Returns the status code (0 = success); see include/sp_region.h."""
+    parr = (ctypes.c_void_p * max(1, len(P)))(*[_ptr(x) for x in P])
+    return load().sp_region_fwd(ctypes.byref(desc), parr, _ptr(residual), _ptr(gamma), _ptr(beta),
+                                _ptr(h_out), _ptr(y_out), _ptr(mask_out), _ptr(mean_out),
+                                _ptr(rstd_out), _stream(stream))
+
+
+def sp_region_bwd(desc, dY, h, mask, mean, rstd, gamma, dR, d_residual, dP, dgamma, dbeta,
+                  workspace, workspace_bytes, stream=None):
+    """Returns the status code (0 = success); see include/sp_region.h."""
+    return load().sp_region_bwd(ctypes.byref(desc), _ptr(dY), _ptr(h), _ptr(mask), _ptr(mean),
+                                _ptr(rstd), _ptr(gamma), _ptr(dR), _ptr(d_residual), _ptr(dP),
+                                _ptr(dgamma), _ptr(dbeta), _ptr(workspace), workspace_bytes,
+                                _stream(stream))
+
+
+# ---- convenience wrappers: allocate outputs with torch, raise on error ----
+
+def _act_dtype(desc):
+    import torch
+    return torch.bfloat16 if desc.dtype == SP_BF16 else torch.float32
+
+
+def forward(desc, P, residual, gamma, beta=None, stream=None):
+    """P: T full [S,B,H] device tensors; residual: the shard (R*H elements).
+    Returns dict h, y, mask, mean (None for RMSNorm), rstd."""
+    import torch
+    dev = residual.device
+    R, H = desc.R, desc.H
+    act = _act_dtype(desc)
+    out = {
+        "h": torch.empty((R, H), dtype=act, device=dev),
+        "y": torch.empty((R, H), dtype=act, device=dev),
+        "mask": torch.empty((R, H), dtype=torch.uint8, device=dev),
+        "mean": torch.empty(R, dtype=torch.float32, device=dev) if desc.norm == SP_LAYERNORM else None,
+        "rstd": torch.empty(R, dtype=torch.float32, device=dev),
+    }
+    _check(sp_region_fwd(desc, P, residual, gamma, beta, out["h"], out["y"], out["mask"],
+                         out["mean"], out["rstd"], stream))
+    return out
+
+
+def backward(desc, dY, h, mask, mean, rstd, gamma, dR=None, workspace=None, stream=None):
+    """Returns dict d_res, dP, dgamma, dbeta (None for RMSNorm)."""
+    import torch
+    dev = dY.device
+    R, H = desc.R, desc.H
+    act = _act_dtype(desc)
+    ws_bytes = sp_region_bwd_workspace_size(desc)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    out = {
+        "d_res": torch.empty((R, H), dtype=act, device=dev),
+        "dP": torch.empty((R, H), dtype=act, device=dev),
+        "dgamma": torch.empty(H, dtype=torch.float32, device=dev),
+        "dbeta": torch.empty(H, dtype=torch.float32, device=dev) if desc.norm == SP_LAYERNORM else None,
+    }
+    _check(sp_region_bwd(desc, dY, h, mask, mean, rstd, gamma, dR, out["d_res"], out["dP"],
+                         out["dgamma"], out["dbeta"], workspace, workspace.numel(), stream))
+    return out
+
+
+class PreparedCall:
+    """A C entry point with its arguments marshalled once, for tight timing loops.
+    Calling it returns nothing and raises on a nonzero status."""
+
+    def __init__(self, fn, args, keep):
+        self._fn = fn
+        self._args = args
+        self._keep = keep  # keeps ctypes objects and tensors alive
+
+    def __call__(self):
+        rc = self._fn(*self._args)
+        if rc != SP_OK:
+            _check(rc)
+
+
+def prepare_fwd(desc, P, residual, gamma, beta, h_out, y_out, mask_out, mean_out, rstd_out,
+                stream=None):
+    L = load()
+    d = SpDesc.from_buffer_copy(desc)
+    parr = (ctypes.c_void_p * len(P))(*[_ptr(x) for x in P])
+    vp = ctypes.c_void_p
+    args = (ctypes.byref(d), parr, vp(_ptr(residual)), vp(_ptr(gamma)), vp(_ptr(beta)),
+            vp(_ptr(h_out)), vp(_ptr(y_out)), vp(_ptr(mask_out)), vp(_ptr(mean_out)),
+            vp(_ptr(rstd_out)), vp(_stream(stream)))
+    return PreparedCall(L.sp_region_fwd, args, (d, parr, P, residual, gamma, beta, h_out, y_out,
+                                                mask_out, mean_out, rstd_out))
+
+
+def prepare_bwd(desc, dY, h, mask, mean, rstd, gamma, dR, d_residual, dP, dgamma, dbeta,
+                workspace, workspace_bytes, stream=None):
+    L = load()
+    d = SpDesc.from_buffer_copy(desc)
+    vp = ctypes.c_void_p
+    args = (ctypes.byref(d), vp(_ptr(dY)), vp(_ptr(h)), vp(_ptr(mask)), vp(_ptr(mean)),
+            vp(_ptr(rstd)), vp(_ptr(gamma)), vp(_ptr(dR)), vp(_ptr(d_residual)), vp(_ptr(dP)),
+            vp(_ptr(dgamma)), vp(_ptr(dbeta)), vp(_ptr(workspace)), ctypes.c_size_t(workspace_bytes),
+            vp(_stream(stream)))
+    return PreparedCall(L.sp_region_bwd, args, (d, dY, h, mask, mean, rstd, gamma, dR, d_residual,
+                                                dP, dgamma, dbeta, workspace))

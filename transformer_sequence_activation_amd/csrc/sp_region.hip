@@ -1,0 +1,998 @@
+// sp_region.hip -- sequence-parallel region kernels for MI355X (gfx950, CDNA4).
+//
+// What is computed is defined in include/sp_region.h (with the passages of the
+// pages it follows).  This file is the device code and the C-ABI host side.
+//
+// Design (gfx950):
+//   * One HBM pass per direction.  A token row of H elements is owned by a
+//     "row group" of TPR lanes (16..64 lanes of one wavefront, or 8..16 whole
+//     wavefronts); each lane owns CPT 16-byte chunks of the row (8 bf16 or 4
+//     fp32 elements), so every global load and store is a coalesced dwordx4.
+//   * All T partial chunks and the residual chunk are loaded before any of them
+//     is used, so a lane keeps (T+1)*CPT 16-byte loads in flight.
+//   * The row statistics are reduced in registers: DPP quad_perm / row mirrors
+//     inside 16-lane rows, ds_swizzle across 32 lanes, ds_bpermute across the
+//     wavefront, and a few LDS words only when a row spans several wavefronts.
+//     Every lane of a row ends with bit-identical statistics.
+//   * The dropout mask is a counter-based Philox4x32-10 keyed on (seed, global
+//     element index): one generator call gives the four words of four
+//     consecutive elements, so a bf16 chunk costs two calls and no state is
+//     kept between launches.
+//   * The backward accumulates dgamma/dbeta for its columns in registers over a
+//     tile of rows, combines the row groups of a workgroup in LDS, writes one
+//     fp32 partial row per workgroup, and a second small kernel sums those
+//     partials in a fixed order: no float atomics, results are run-to-run
+//     identical.
+//   * No MFMA: nothing here is a contraction; the path is bound by HBM.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "sp_region.h"
+
+#ifndef SP_BWD_TARGET_BLOCKS
+#define SP_BWD_TARGET_BLOCKS 256  // workgroups the backward aims for (tiles of rows)
+#endif
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Activation element types: a 16-byte chunk holds E elements.
+
+template <int DT>
+struct Act;
+
+template <>
+struct Act<SP_BF16> {
+    static constexpr int E = 8;
+    static constexpr int kBytes = 2;
+    static __device__ __forceinline__ void unpack(const u32x4 v, float (&f)[8]) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            f[2 * m] = __uint_as_float(v[m] << 16);
+            f[2 * m + 1] = __uint_as_float(v[m] & 0xFFFF0000u);
+        }
+    }
+    // fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 under the default
+    // rounding mode), two elements per instruction.
+    static __device__ __forceinline__ u32x4 pack(const float (&f)[8]) {
+        u32x4 v;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            f32x2 pr = {f[2 * m], f[2 * m + 1]};
+            v[m] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
+        }
+        return v;
+    }
+};
+
+template <>
+struct Act<SP_F32> {
+    static constexpr int E = 4;
+    static constexpr int kBytes = 4;
+    static __device__ __forceinline__ void unpack(const u32x4 v, float (&f)[4]) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) f[m] = __uint_as_float(v[m]);
+    }
+    static __device__ __forceinline__ u32x4 pack(const float (&f)[4]) {
+        u32x4 v;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) v[m] = __float_as_uint(f[m]);
+        return v;
+    }
+};
+
+__device__ __forceinline__ u32x4 ld16(const void* base, int64_t byte_off) {
+    return *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(base) + byte_off);
+}
+__device__ __forceinline__ void st16(void* base, int64_t byte_off, u32x4 v) {
+    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(base) + byte_off) = v;
+}
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two 32x32->64
+// multiplies whose halves are mixed into the other counter words with the round
+// key; the key advances by two Weyl constants between rounds.  Counter words 2
+// and 3 are zero here.
+
+constexpr uint32_t kPhiloxM0 = 0xD2511F53u;
+constexpr uint32_t kPhiloxM1 = 0xCD9E8D57u;
+constexpr uint32_t kPhiloxW0 = 0x9E3779B9u;
+constexpr uint32_t kPhiloxW1 = 0xBB67AE85u;
+
+__device__ __forceinline__ void philox10(uint32_t c0, uint32_t c1, uint32_t k0, uint32_t k1,
+                                         uint32_t (&w)[4]) {
+    uint32_t x0 = c0, x1 = c1, x2 = 0u, x3 = 0u;
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) {
+            k0 += kPhiloxW0;
+            k1 += kPhiloxW1;
+        }
+        const uint64_t p0 = (uint64_t)kPhiloxM0 * x0;
+        const uint64_t p1 = (uint64_t)kPhiloxM1 * x2;
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ x1 ^ k0;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ x3 ^ k1;
+        x1 = (uint32_t)p1;
+        x3 = (uint32_t)p0;
+        x0 = n0;
+        x2 = n2;
+    }
+    w[0] = x0;
+    w[1] = x1;
+    w[2] = x2;
+    w[3] = x3;
+}
+
+// Keep flags of the E elements starting at global index gi0 (a multiple of E).
+template <int E>
+__device__ __forceinline__ void keep_flags(uint64_t gi0, uint32_t thr, uint32_t k0, uint32_t k1,
+                                           bool (&keep)[E]) {
+#pragma unroll
+    for (int q = 0; q < E / 4; ++q) {
+        const uint64_t c = (gi0 >> 2) + (uint64_t)q;
+        uint32_t w[4];
+        philox10((uint32_t)c, (uint32_t)(c >> 32), k0, k1, w);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) keep[4 * q + m] = w[m] >= thr;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Reductions over a row group of TPR lanes; every lane gets the same bits.
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+template <int TPR>
+__device__ __forceinline__ float lanes_sum(float v) {
+    static_assert(TPR >= 16, "row groups span at least one 16-lane DPP row");
+    v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]: lane ^ 1
+    v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]: lane ^ 2
+    v += dpp<0x141>(v);  // row_half_mirror: the other quad of the 8
+    v += dpp<0x140>(v);  // row_mirror: the other 8 of the 16
+    if constexpr (TPR >= 32)
+        v += __builtin_bit_cast(
+            float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));  // lane ^ 16
+    if constexpr (TPR >= 64) v += __shfl_xor(v, 32);
+    return v;
+}
+
+// Sum NV values over the TPR lanes of each row group of a BLOCK-thread block.
+// Must be reached by every thread of the block (it may synchronise).
+template <int TPR, int BLOCK, int NV>
+__device__ __forceinline__ void group_sum(float (&v)[NV]) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) v[i] = lanes_sum<TPR>(v[i]);
+    if constexpr (TPR > kWave) {
+        constexpr int NW = TPR / kWave;
+        constexpr int RPW = BLOCK / TPR;
+        __shared__ float red[RPW * NW * NV];
+        const int tid = threadIdx.x;
+        const int rg = tid / TPR;
+        const int w = (tid % TPR) / kWave;
+        if ((tid & (kWave - 1)) == 0) {
+#pragma unroll
+            for (int i = 0; i < NV; ++i) red[(rg * NW + w) * NV + i] = v[i];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            float s = red[(rg * NW) * NV + i];
+#pragma unroll
+            for (int q = 1; q < NW; ++q) s += red[(rg * NW + q) * NV + i];
+            v[i] = s;
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Forward.
+
+struct FwdArgs {
+    const void* P[SP_MAX_T];  // each points at the first element of shard j of P_t
+    const void* residual;
+    const float* gamma;
+    const float* beta;
+    void* h;
+    void* y;
+    uint8_t* mask;
+    float* mean;
+    float* rstd;
+    int64_t R;       // token rows in the shard
+    uint64_t base;   // global index of the shard's first element (j * R * H)
+    int32_t H;
+    int32_t nchunk;  // H / E
+    int32_t T;
+    int32_t norm;
+    uint32_t thr;    // keep iff word >= thr
+    uint32_t key0, key1;
+    float scale;     // 1 / (1 - p) in fp32
+    float eps;
+    float inv_h;
+};
+
+// h = round(residual + (keep ? sum * scale : +0)), fp32 and unfused, so that
+// the product and the sum each round once.
+template <int E>
+__device__ __forceinline__ void residual_add(const float (&acc)[E], const float (&res)[E],
+                                             const bool (&keep)[E], float scale, float (&hf)[E]) {
+#pragma clang fp contract(off)
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const float z = keep[e] ? acc[e] * scale : 0.0f;
+        hf[e] = res[e] + z;
+    }
+}
+
+template <int E>
+struct MaskWord;
+template <>
+struct MaskWord<8> {
+    typedef uint2 type;
+    static __device__ __forceinline__ uint2 make(const bool (&k)[8]) {
+        uint2 m;
+        m.x = (uint32_t)k[0] | ((uint32_t)k[1] << 8) | ((uint32_t)k[2] << 16) | ((uint32_t)k[3] << 24);
+        m.y = (uint32_t)k[4] | ((uint32_t)k[5] << 8) | ((uint32_t)k[6] << 16) | ((uint32_t)k[7] << 24);
+        return m;
+    }
+    static __device__ __forceinline__ void unmake(uint2 m, bool (&k)[8]) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            k[e] = (m.x >> (8 * e)) & 0xFFu;
+            k[4 + e] = (m.y >> (8 * e)) & 0xFFu;
+        }
+    }
+};
+template <>
+struct MaskWord<4> {
+    typedef uint32_t type;
+    static __device__ __forceinline__ uint32_t make(const bool (&k)[4]) {
+        return (uint32_t)k[0] | ((uint32_t)k[1] << 8) | ((uint32_t)k[2] << 16) | ((uint32_t)k[3] << 24);
+    }
+    static __device__ __forceinline__ void unmake(uint32_t m, bool (&k)[4]) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) k[e] = (m >> (8 * e)) & 0xFFu;
+    }
+};
+
+template <int E>
+__device__ __forceinline__ void load_vec_f32(const float* p, int64_t idx, float (&f)[E]) {
+#pragma unroll
+    for (int q = 0; q < E / 4; ++q) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(p + idx + 4 * q);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) f[4 * q + m] = v[m];
+    }
+}
+
+// TT: number of partials fixed at compile time (0 = read a.T at run time).
+template <int DT, int TT, int TPR, int CPT, int BLOCK>
+__global__ __launch_bounds__(BLOCK) void sp_fwd_kernel(const FwdArgs a) {
+    using A = Act<DT>;
+    constexpr int E = A::E;
+    constexpr int EB = A::kBytes;
+    constexpr int RPW = BLOCK / TPR;
+    using MW = MaskWord<E>;
+
+    const int tid = threadIdx.x;
+    const int rg = tid / TPR;
+    const int l = tid % TPR;
+    const int64_t row = (int64_t)blockIdx.x * RPW + rg;
+    const bool row_ok = row < a.R;
+    const int64_t rowc = row_ok ? row : a.R - 1;  // loads stay in bounds; stores are predicated
+    const int64_t row_elem = rowc * (int64_t)a.H;
+
+    int col[CPT];
+    bool ok[CPT];
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+        const int c = l + k * TPR;
+        ok[k] = c < a.nchunk;
+        col[k] = (ok[k] ? c : a.nchunk - 1) * E;
+    }
+
+    // ---- loads: every partial chunk and the residual, issued together ----
+    float acc[CPT][E];
+    float res[CPT][E];
+    if constexpr (TT > 0) {
+        u32x4 pv[CPT][TT];
+        u32x4 rv[CPT];
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) {
+            const int64_t off = (row_elem + col[k]) * EB;
+#pragma unroll
+            for (int t = 0; t < TT; ++t) pv[k][t] = ld16(a.P[t], off);
+            rv[k] = ld16(a.residual, off);
+        }
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) {
+            A::unpack(pv[k][0], acc[k]);
+#pragma unroll
+            for (int t = 1; t < TT; ++t) {
+                float f[E];
+                A::unpack(pv[k][t], f);
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[k][e] = acc[k][e] + f[e];
+            }
+            A::unpack(rv[k], res[k]);
+        }
+    } else {
+        u32x4 rv[CPT];
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) {
+            const int64_t off = (row_elem + col[k]) * EB;
+            rv[k] = ld16(a.residual, off);
+            A::unpack(ld16(a.P[0], off), acc[k]);
+        }
+        for (int t = 1; t < a.T; ++t) {
+#pragma unroll
+            for (int k = 0; k < CPT; ++k) {
+                float f[E];
+                A::unpack(ld16(a.P[t], (row_elem + col[k]) * EB), f);
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[k][e] = acc[k][e] + f[e];
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) A::unpack(rv[k], res[k]);
+    }
+
+    // gamma / beta for the normalisation, loaded early
+    float gam[CPT][E], bet[CPT][E];
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+        load_vec_f32<E>(a.gamma, col[k], gam[k]);
+        if (a.norm == SP_LAYERNORM) load_vec_f32<E>(a.beta, col[k], bet[k]);
+    }
+
+    // ---- dropout + residual add, one rounding of h ----
+    float hv[CPT][E];
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+        const int64_t idx = row_elem + col[k];
+        bool keep[E];
+        keep_flags<E>(a.base + (uint64_t)idx, a.thr, a.key0, a.key1, keep);
+        float hf[E];
+        residual_add<E>(acc[k], res[k], keep, a.scale, hf);
+        const u32x4 hp = A::pack(hf);
+        A::unpack(hp, hv[k]);  // the rounded h the norm sees
+        if (row_ok && ok[k]) {
+            st16(a.h, idx * EB, hp);
+            *reinterpret_cast<typename MW::type*>(a.mask + idx) = MW::make(keep);
+        }
+    }
+
+    // ---- per-token statistics ----
+    float mu = 0.0f, rs;
+    if (a.norm == SP_LAYERNORM) {
+        float s[1] = {0.0f};
+#pragma unroll
+        for (int k = 0; k < CPT; ++k)
+            if (ok[k])
+#pragma unroll
+                for (int e = 0; e < E; ++e) s[0] += hv[k][e];
+        group_sum<TPR, BLOCK, 1>(s);
+        mu = s[0] * a.inv_h;
+        float q[1] = {0.0f};
+#pragma unroll
+        for (int k = 0; k < CPT; ++k)
+            if (ok[k])
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float dlt = hv[k][e] - mu;
+                    q[0] += dlt * dlt;
+                }
+        group_sum<TPR, BLOCK, 1>(q);
+        rs = rsqrtf(q[0] * a.inv_h + a.eps);
+    } else {
+        float q[1] = {0.0f};
+#pragma unroll
+        for (int k = 0; k < CPT; ++k)
+            if (ok[k])
+#pragma unroll
+                for (int e = 0; e < E; ++e) q[0] += hv[k][e] * hv[k][e];
+        group_sum<TPR, BLOCK, 1>(q);
+        rs = rsqrtf(q[0] * a.inv_h + a.eps);
+    }
+
+    // ---- y = gamma * xhat (+ beta), one rounding ----
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+        float yv[E];
+        if (a.norm == SP_LAYERNORM) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) yv[e] = gam[k][e] * ((hv[k][e] - mu) * rs) + bet[k][e];
+        } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) yv[e] = gam[k][e] * (hv[k][e] * rs);
+        }
+        if (row_ok && ok[k]) st16(a.y, (row_elem + col[k]) * EB, A::pack(yv));
+    }
+    if (row_ok && l == 0) {
+        a.rstd[row] = rs;
+        if (a.norm == SP_LAYERNORM) a.mean[row] = mu;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Backward.
+
+struct BwdArgs {
+    const void* dY;
+    const void* h;
+    const uint8_t* mask;
+    const float* mean;
+    const float* rstd;
+    const float* gamma;
+    const void* dR;
+    void* dres;
+    void* dP;
+    float* ws;            // [G][nacc][H] fp32 partial sums of dgamma (, dbeta)
+    int64_t R;
+    int64_t rows_per_block;
+    int32_t H;
+    int32_t nchunk;
+    int32_t norm;
+    int32_t nacc;         // 1 (RMSNorm) or 2 (LayerNorm)
+    float scale;
+    float inv_h;
+};
+
+template <int DT, int CPT, int E>
+struct BwdRow {
+    u32x4 dy[CPT];
+    u32x4 hh[CPT];
+    u32x4 dr[CPT];
+    typename MaskWord<E>::type m[CPT];
+    float mu, rs;
+};
+
+template <int DT, int TPR, int CPT, int BLOCK, bool HAS_DR>
+__device__ __forceinline__ void bwd_load(const BwdArgs& a, int64_t rowc, const int (&col)[CPT],
+                                         BwdRow<DT, CPT, Act<DT>::E>& b) {
+    using A = Act<DT>;
+    constexpr int E = A::E;
+    constexpr int EB = A::kBytes;
+    const int64_t row_elem = rowc * (int64_t)a.H;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+        const int64_t idx = row_elem + col[k];
+        b.dy[k] = ld16(a.dY, idx * EB);
+        b.hh[k] = ld16(a.h, idx * EB);
+        if constexpr (HAS_DR) b.dr[k] = ld16(a.dR, idx * EB);
+        b.m[k] = *reinterpret_cast<const typename MaskWord<E>::type*>(a.mask + idx);
+    }
+    b.rs = a.rstd[rowc];
+    b.mu = (a.norm == SP_LAYERNORM) ? a.mean[rowc] : 0.0f;
+}
+
+template <int DT, int TPR, int CPT, int BLOCK, bool HAS_DR>
+__global__ __launch_bounds__(BLOCK) void sp_bwd_kernel(const BwdArgs a) {
+    using A = Act<DT>;
+    constexpr int E = A::E;
+    constexpr int EB = A::kBytes;
+    constexpr int RPW = BLOCK / TPR;
+    using MW = MaskWord<E>;
+    extern __shared__ float comb[];  // [RPW][nacc][H] when RPW > 1
+
+    const int tid = threadIdx.x;
+    const int rg = tid / TPR;
+    const int l = tid % TPR;
+    const bool ln = a.norm == SP_LAYERNORM;
+    const int64_t row_begin = (int64_t)blockIdx.x * a.rows_per_block;
+    const int64_t row_end = min(row_begin + a.rows_per_block, a.R);
+    const int iters = (int)((a.rows_per_block + RPW - 1) / RPW);  // uniform over the grid
+
+    int col[CPT];
+    bool ok[CPT];
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+        const int c = l + k * TPR;
+        ok[k] = c < a.nchunk;
+        col[k] = (ok[k] ? c : a.nchunk - 1) * E;
+    }
+    float gam[CPT][E];
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) load_vec_f32<E>(a.gamma, col[k], gam[k]);
+
+    float dg[CPT][E], db[CPT][E];
+#pragma unroll
+    for (int k = 0; k < CPT; ++k)
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            dg[k][e] = 0.0f;
+            db[k][e] = 0.0f;
+        }
+
+    BwdRow<DT, CPT, E> cur, nxt;
+    {
+        const int64_t r = row_begin + rg;
+        bwd_load<DT, TPR, CPT, BLOCK, HAS_DR>(a, r < row_end ? r : a.R - 1, col, cur);
+    }
+    for (int it = 0; it < iters; ++it) {
+        const int64_t row = row_begin + (int64_t)it * RPW + rg;
+        const bool row_ok = row < row_end;
+        // prefetch the next row of this row group while this one is computed
+        if (it + 1 < iters) {
+            const int64_t rn = row + RPW;
+            bwd_load<DT, TPR, CPT, BLOCK, HAS_DR>(a, rn < row_end ? rn : a.R - 1, col, nxt);
+        }
+        float xh[CPT][E], g[CPT][E], dyv[CPT][E];
+        float s[2] = {0.0f, 0.0f};
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) {
+            float hv[E];
+            A::unpack(cur.dy[k], dyv[k]);
+            A::unpack(cur.hh[k], hv);
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                xh[k][e] = (hv[e] - cur.mu) * cur.rs;
+                g[k][e] = dyv[k][e] * gam[k][e];
+            }
+            if (ok[k]) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    s[0] += g[k][e];
+                    s[1] += g[k][e] * xh[k][e];
+                }
+                if (row_ok) {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        dg[k][e] += dyv[k][e] * xh[k][e];
+                        db[k][e] += dyv[k][e];
+                    }
+                }
+            }
+        }
+        group_sum<TPR, BLOCK, 2>(s);
+        const float c1 = ln ? s[0] * a.inv_h : 0.0f;
+        const float c2 = s[1] * a.inv_h;
+        const int64_t row_elem = (row_ok ? row : 0) * (int64_t)a.H;
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) {
+            float dh[E], dp[E];
+            bool keep[E];
+            MW::unmake(cur.m[k], keep);
+            float drv[E];
+            if constexpr (HAS_DR) A::unpack(cur.dr[k], drv);
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                float v = cur.rs * (g[k][e] - c1 - xh[k][e] * c2);
+                if constexpr (HAS_DR) v += drv[e];
+                dh[e] = v;
+                dp[e] = keep[e] ? v * a.scale : 0.0f;
+            }
+            if (row_ok && ok[k]) {
+                const int64_t off = (row_elem + col[k]) * EB;
+                st16(a.dres, off, A::pack(dh));
+                st16(a.dP, off, A::pack(dp));
+            }
+        }
+        if (it + 1 < iters) cur = nxt;
+    }
+
+    // ---- this workgroup's partial dgamma / dbeta row ----
+    float* out = a.ws + (int64_t)blockIdx.x * a.nacc * a.H;
+    if constexpr (RPW == 1) {
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) {
+            if (!ok[k]) continue;
+#pragma unroll
+            for (int q = 0; q < E / 4; ++q) {
+                f32x4 v = {dg[k][4 * q], dg[k][4 * q + 1], dg[k][4 * q + 2], dg[k][4 * q + 3]};
+                *reinterpret_cast<f32x4*>(out + col[k] + 4 * q) = v;
+                if (ln) {
+                    f32x4 w = {db[k][4 * q], db[k][4 * q + 1], db[k][4 * q + 2], db[k][4 * q + 3]};
+                    *reinterpret_cast<f32x4*>(out + a.H + col[k] + 4 * q) = w;
+                }
+            }
+        }
+    } else {
+        const int H = a.H;
+        float* mine = comb + (int64_t)rg * a.nacc * H;
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) {
+            if (!ok[k]) continue;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                mine[col[k] + e] = dg[k][e];
+                if (ln) mine[H + col[k] + e] = db[k][e];
+            }
+        }
+        __syncthreads();
+        const int n = a.nacc * H;
+        for (int c = tid; c < n; c += BLOCK) {
+            float v = comb[c];
+#pragma unroll
+            for (int q = 1; q < RPW; ++q) v += comb[(int64_t)q * n + c];
+            out[c] = v;
+        }
+    }
+}
+
+// dgamma[k] (and dbeta[k]) = sum over the G workgroup partials, in a fixed
+// order: four lanes split the partials into contiguous quarters and the
+// quarters are added in order.
+constexpr int kFinCols = 64;
+constexpr int kFinSplit = 4;
+
+__global__ __launch_bounds__(kFinCols* kFinSplit) void sp_dgamma_finish_kernel(
+    const float* ws, int64_t G, int32_t H, int32_t nacc, float* dgamma, float* dbeta) {
+    __shared__ float part[kFinSplit][kFinCols];
+    const int n = nacc * H;
+    const int ci = threadIdx.x % kFinCols;
+    const int sp = threadIdx.x / kFinCols;
+    const int c = blockIdx.x * kFinCols + ci;
+    const int64_t per = (G + kFinSplit - 1) / kFinSplit;
+    const int64_t g0 = sp * per;
+    const int64_t g1 = min(g0 + per, G);
+    float v = 0.0f;
+    if (c < n) {
+        for (int64_t g = g0; g < g1; ++g) v += ws[g * n + c];
+    }
+    part[sp][ci] = v;
+    __syncthreads();
+    if (sp == 0 && c < n) {
+        float s = part[0][ci];
+#pragma unroll
+        for (int q = 1; q < kFinSplit; ++q) s += part[q][ci];
+        if (c < H) dgamma[c] = s;
+        else dbeta[c - H] = s;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launch layouts: (lanes per row, chunks per lane) by row length in chunks.
+
+struct Layout {
+    int tpr, cpt, max_chunks;
+};
+constexpr Layout kLayouts[] = {
+    {16, 1, 16},   {32, 1, 32},   {64, 1, 64},  {32, 3, 96},   {64, 2, 128},   {64, 3, 192},
+    {64, 4, 256},  {512, 1, 512}, {512, 2, 1024}, {512, 4, 2048}, {1024, 4, 4096}, {1024, 8, 8192},
+};
+constexpr int kNumLayouts = sizeof(kLayouts) / sizeof(kLayouts[0]);
+constexpr int kSubWaveBlock = 256;  // block size of the layouts whose rows fit in one wavefront
+
+constexpr int block_of(int tpr) { return tpr <= kWave ? kSubWaveBlock : tpr; }
+
+typedef void (*FwdKernel)(FwdArgs);
+typedef void (*BwdKernel)(BwdArgs);
+
+#define SP_LAYOUT_LIST(X, ...)                                                                    \
+    X(16, 1, __VA_ARGS__), X(32, 1, __VA_ARGS__), X(64, 1, __VA_ARGS__), X(32, 3, __VA_ARGS__),   \
+        X(64, 2, __VA_ARGS__), X(64, 3, __VA_ARGS__), X(64, 4, __VA_ARGS__),                      \
+        X(512, 1, __VA_ARGS__), X(512, 2, __VA_ARGS__), X(512, 4, __VA_ARGS__),                   \
+        X(1024, 4, __VA_ARGS__), X(1024, 8, __VA_ARGS__)
+
+#define SP_FWD_ENTRY(TPR, CPT, DT, TT) &sp_fwd_kernel<DT, TT, TPR, CPT, block_of(TPR)>
+#define SP_BWD_ENTRY(TPR, CPT, DT, HDR) &sp_bwd_kernel<DT, TPR, CPT, block_of(TPR), HDR>
+
+const FwdKernel kFwdBf16[5][kNumLayouts] = {
+    {SP_LAYOUT_LIST(SP_FWD_ENTRY, SP_BF16, 0)}, {SP_LAYOUT_LIST(SP_FWD_ENTRY, SP_BF16, 1)},
+    {SP_LAYOUT_LIST(SP_FWD_ENTRY, SP_BF16, 2)}, {SP_LAYOUT_LIST(SP_FWD_ENTRY, SP_BF16, 4)},
+    {SP_LAYOUT_LIST(SP_FWD_ENTRY, SP_BF16, 8)},
+};
+const FwdKernel kFwdF32[kNumLayouts] = {SP_LAYOUT_LIST(SP_FWD_ENTRY, SP_F32, 0)};
+const BwdKernel kBwd[2][2][kNumLayouts] = {
+    {{SP_LAYOUT_LIST(SP_BWD_ENTRY, SP_F32, false)}, {SP_LAYOUT_LIST(SP_BWD_ENTRY, SP_F32, true)}},
+    {{SP_LAYOUT_LIST(SP_BWD_ENTRY, SP_BF16, false)}, {SP_LAYOUT_LIST(SP_BWD_ENTRY, SP_BF16, true)}},
+};
+
+// ---------------------------------------------------------------------------
+// Host-side validation.
+
+thread_local char g_hip_error[256] = "no HIP error recorded";
+
+inline int elem_bytes(int dtype) { return dtype == SP_BF16 ? 2 : 4; }
+inline int elems_per_chunk(int dtype) { return 16 / elem_bytes(dtype); }
+
+int check_desc(const sp_desc_t* d) {
+    if (!d) return SP_EINVAL;
+    if (d->dtype != SP_F32 && d->dtype != SP_BF16) return SP_EDTYPE;
+    if (d->norm != SP_RMSNORM && d->norm != SP_LAYERNORM) return SP_EPARAM;
+    if (!(d->p >= 0.0f && d->p < 1.0f)) return SP_EPARAM;
+    if (!(d->eps >= 0.0f) || !isfinite(d->eps)) return SP_EPARAM;
+    if (d->S < 0 || d->B < 0 || d->H <= 0) return SP_ESHAPE;
+    if (d->T < 1 || d->T > SP_MAX_T) return SP_ESHAPE;
+    if (d->j < 0 || d->j >= d->T) return SP_ESHAPE;
+    if (d->S % d->T != 0) return SP_ESHAPE;
+    const int64_t eb = elem_bytes(d->dtype);
+    if ((d->H * eb) % 16 != 0 || d->H * eb > SP_MAX_H_BYTES) return SP_ESHAPE;
+    // element indices of the full tensor must fit in 63 bits
+    if (d->S > 0 && d->B > 0 && (d->B > INT64_MAX / d->S || d->S * d->B > INT64_MAX / d->H / eb))
+        return SP_ESHAPE;
+    return SP_OK;
+}
+
+inline int64_t shard_rows(const sp_desc_t* d) { return (d->S / d->T) * d->B; }
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Span {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+inline Span span(const void* p, int64_t bytes) {
+    return Span{(uintptr_t)p, (uintptr_t)p + (uintptr_t)(bytes > 0 ? bytes : 0)};
+}
+inline bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+
+// Every output span against every other span.
+bool any_overlap(const Span* outs, int nout, const Span* ins, int nin) {
+    for (int i = 0; i < nout; ++i) {
+        for (int k = i + 1; k < nout; ++k)
+            if (overlap(outs[i], outs[k])) return true;
+        for (int k = 0; k < nin; ++k)
+            if (overlap(outs[i], ins[k])) return true;
+    }
+    return false;
+}
+
+int pick_layout(int64_t nchunk) {
+    for (int i = 0; i < kNumLayouts; ++i)
+        if (nchunk <= kLayouts[i].max_chunks) return i;
+    return -1;
+}
+
+int fwd_tt_index(int T) {
+    switch (T) {
+        case 1: return 1;
+        case 2: return 2;
+        case 4: return 3;
+        case 8: return 4;
+        default: return 0;
+    }
+}
+
+struct BwdPlan {
+    int layout;
+    int64_t rows_per_block;
+    int64_t blocks;
+    int nacc;
+    size_t ws_bytes;
+    size_t lds_bytes;
+};
+
+BwdPlan plan_bwd(const sp_desc_t* d) {
+    BwdPlan p{};
+    const int64_t R = shard_rows(d);
+    const int64_t nchunk = d->H / elems_per_chunk(d->dtype);
+    p.layout = pick_layout(nchunk);
+    const int tpr = kLayouts[p.layout].tpr;
+    const int rpw = block_of(tpr) / tpr;
+    p.nacc = d->norm == SP_LAYERNORM ? 2 : 1;
+    int64_t rpb = (R + SP_BWD_TARGET_BLOCKS - 1) / SP_BWD_TARGET_BLOCKS;
+    rpb = ((rpb + rpw - 1) / rpw) * rpw;
+    if (rpb < rpw) rpb = rpw;
+    p.rows_per_block = rpb;
+    p.blocks = R > 0 ? (R + rpb - 1) / rpb : 0;
+    p.ws_bytes = (size_t)p.blocks * (size_t)p.nacc * (size_t)d->H * sizeof(float);
+    p.lds_bytes = rpw > 1 ? (size_t)rpw * (size_t)p.nacc * (size_t)d->H * sizeof(float) : 0;
+    return p;
+}
+
+int record_hip(hipError_t e) {
+    snprintf(g_hip_error, sizeof(g_hip_error), "HIP error %d: %s", (int)e, hipGetErrorString(e));
+    return SP_EHIP;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI.
+
+extern "C" int sp_region_version(void) { return 100; }
+
+extern "C" const char* sp_region_strerror(int status) {
+    switch (status) {
+        case SP_OK: return "success";
+        case SP_EINVAL: return "invalid, missing or overlapping pointer argument";
+        case SP_ESHAPE: return "invalid shape (S, B, H, T or j)";
+        case SP_EDTYPE: return "unknown activation dtype";
+        case SP_EPARAM: return "invalid norm, dropout probability or eps";
+        case SP_EALIGN: return "tensor pointer not 16-byte aligned";
+        case SP_EWORKSPACE: return "workspace missing or smaller than sp_region_bwd_workspace_size";
+        case SP_EHIP: return g_hip_error;
+        default: return "unknown status";
+    }
+}
+
+extern "C" int sp_region_traffic_bytes(const sp_desc_t* d, uint64_t* fwd_bytes, uint64_t* bwd_bytes) {
+    const int rc = check_desc(d);
+    if (rc != SP_OK) return rc;
+    if (!fwd_bytes || !bwd_bytes) return SP_EINVAL;
+    const uint64_t R = (uint64_t)shard_rows(d), H = (uint64_t)d->H, T = (uint64_t)d->T;
+    const uint64_t N = R * H, e = (uint64_t)elem_bytes(d->dtype);
+    const uint64_t ln = d->norm == SP_LAYERNORM ? 1 : 0;
+    const uint64_t stats = R * 4 * (1 + ln);    // rstd (+ mean)
+    const uint64_t params = H * 4 * (1 + ln);   // gamma (+ beta) / dgamma (+ dbeta)
+    // fwd: T partial slabs + residual in; h, y, mask, stats out; gamma/beta in
+    *fwd_bytes = T * N * e + N * e + N * e + N * e + N + stats + params;
+    // bwd: dY, h, mask, stats, gamma in; d_residual, dP, dgamma/dbeta out
+    *bwd_bytes = N * e + N * e + N + stats + H * 4 + N * e + N * e + params;
+    return SP_OK;
+}
+
+extern "C" size_t sp_region_bwd_workspace_size(const sp_desc_t* d) {
+    if (check_desc(d) != SP_OK) return 0;
+    return plan_bwd(d).ws_bytes;
+}
+
+extern "C" int sp_region_fwd(const sp_desc_t* d, const void* const* P, const void* residual,
+                             const float* gamma, const float* beta, void* h_out, void* y_out,
+                             uint8_t* mask_out, float* mean_out, float* rstd_out, void* stream) {
+    int rc = check_desc(d);
+    if (rc != SP_OK) return rc;
+    const bool ln = d->norm == SP_LAYERNORM;
+    const int64_t R = shard_rows(d), H = d->H, N = R * H;
+    const int eb = elem_bytes(d->dtype);
+    const int64_t base = (int64_t)d->j * N;
+    // [H] parameters are always required; shard-sized tensors only when the shard has rows
+    if (!gamma || ln != (beta != nullptr)) return SP_EINVAL;
+    if (R > 0) {
+        if (!P || !residual || !h_out || !y_out || !mask_out || !rstd_out) return SP_EINVAL;
+        if (ln != (mean_out != nullptr)) return SP_EINVAL;
+        for (int t = 0; t < d->T; ++t)
+            if (!P[t]) return SP_EINVAL;
+    } else if (!ln && mean_out) {
+        return SP_EINVAL;
+    }
+    if (R > 0)
+        for (int t = 0; t < d->T; ++t)
+            if (!aligned16(P[t])) return SP_EALIGN;
+    if (!aligned16(residual) || !aligned16(gamma) || (beta && !aligned16(beta)) ||
+        !aligned16(h_out) || !aligned16(y_out) || !aligned16(mask_out) ||
+        (mean_out && !aligned16(mean_out)) || !aligned16(rstd_out))
+        return SP_EALIGN;
+    if (R == 0) return SP_OK;
+    Span ins[SP_MAX_T + 3];
+    int nin = 0;
+    for (int t = 0; t < d->T; ++t)
+        ins[nin++] = span((const char*)P[t] + base * eb, N * eb);
+    ins[nin++] = span(residual, N * eb);
+    ins[nin++] = span(gamma, H * 4);
+    if (beta) ins[nin++] = span(beta, H * 4);
+    Span outs[5];
+    int nout = 0;
+    outs[nout++] = span(h_out, N * eb);
+    outs[nout++] = span(y_out, N * eb);
+    outs[nout++] = span(mask_out, N);
+    outs[nout++] = span(rstd_out, R * 4);
+    if (mean_out) outs[nout++] = span(mean_out, R * 4);
+    if (any_overlap(outs, nout, ins, nin)) return SP_EINVAL;
+
+    FwdArgs a;
+    memset(&a, 0, sizeof(a));
+    for (int t = 0; t < d->T; ++t) a.P[t] = (const char*)P[t] + base * eb;
+    a.residual = residual;
+    a.gamma = gamma;
+    a.beta = beta;
+    a.h = h_out;
+    a.y = y_out;
+    a.mask = mask_out;
+    a.mean = mean_out;
+    a.rstd = rstd_out;
+    a.R = R;
+    a.base = (uint64_t)base;
+    a.H = (int32_t)H;
+    a.nchunk = (int32_t)(H / elems_per_chunk(d->dtype));
+    a.T = d->T;
+    a.norm = d->norm;
+    a.thr = (uint32_t)floor((double)d->p * 4294967296.0);
+    a.key0 = (uint32_t)d->seed;
+    a.key1 = (uint32_t)(d->seed >> 32);
+    a.scale = (float)(1.0 / (1.0 - (double)d->p));
+    a.eps = d->eps;
+    a.inv_h = (float)(1.0 / (double)H);
+
+    const int li = pick_layout(a.nchunk);
+    if (li < 0) return SP_ESHAPE;
+    const Layout L = kLayouts[li];
+    const int block = block_of(L.tpr);
+    const int rpw = block / L.tpr;
+    const int64_t grid = (R + rpw - 1) / rpw;
+    if (grid > INT32_MAX) return SP_ESHAPE;
+    const FwdKernel k = d->dtype == SP_BF16 ? kFwdBf16[fwd_tt_index(d->T)][li] : kFwdF32[li];
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(block), 0, (hipStream_t)stream, a);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? SP_OK : record_hip(e);
+}
+
+extern "C" int sp_region_bwd(const sp_desc_t* d, const void* dY, const void* h, const uint8_t* mask,
+                             const float* mean, const float* rstd, const float* gamma, const void* dR,
+                             void* d_residual, void* dP, float* dgamma, float* dbeta, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    int rc = check_desc(d);
+    if (rc != SP_OK) return rc;
+    const bool ln = d->norm == SP_LAYERNORM;
+    // [H] tensors are always required; shard-sized tensors only when the shard has rows
+    if (!gamma || !dgamma || ln != (dbeta != nullptr)) return SP_EINVAL;
+    if (shard_rows(d) > 0) {
+        if (!dY || !h || !mask || !rstd || !d_residual || !dP) return SP_EINVAL;
+        if (ln != (mean != nullptr)) return SP_EINVAL;
+    } else if (!ln && mean) {
+        return SP_EINVAL;
+    }
+    if (!aligned16(dY) || !aligned16(h) || !aligned16(mask) || (mean && !aligned16(mean)) ||
+        !aligned16(rstd) || !aligned16(gamma) || (dR && !aligned16(dR)) || !aligned16(d_residual) ||
+        !aligned16(dP) || !aligned16(dgamma) || (dbeta && !aligned16(dbeta)))
+        return SP_EALIGN;
+    const BwdPlan plan = plan_bwd(d);
+    if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes)) return SP_EWORKSPACE;
+    if (workspace && !aligned16(workspace)) return SP_EALIGN;
+    const int64_t R = shard_rows(d), H = d->H, N = R * H;
+    const int eb = elem_bytes(d->dtype);
+    Span ins[8];
+    int nin = 0;
+    ins[nin++] = span(dY, N * eb);
+    ins[nin++] = span(h, N * eb);
+    ins[nin++] = span(mask, N);
+    ins[nin++] = span(rstd, R * 4);
+    ins[nin++] = span(gamma, H * 4);
+    if (mean) ins[nin++] = span(mean, R * 4);
+    if (dR) ins[nin++] = span(dR, N * eb);
+    Span outs[5];
+    int nout = 0;
+    outs[nout++] = span(d_residual, N * eb);
+    outs[nout++] = span(dP, N * eb);
+    outs[nout++] = span(dgamma, H * 4);
+    if (dbeta) outs[nout++] = span(dbeta, H * 4);
+    if (plan.ws_bytes > 0) outs[nout++] = span(workspace, (int64_t)plan.ws_bytes);
+    if (any_overlap(outs, nout, ins, nin)) return SP_EINVAL;
+
+    BwdArgs a;
+    memset(&a, 0, sizeof(a));
+    a.dY = dY;
+    a.h = h;
+    a.mask = mask;
+    a.mean = mean;
+    a.rstd = rstd;
+    a.gamma = gamma;
+    a.dR = dR;
+    a.dres = d_residual;
+    a.dP = dP;
+    a.ws = (float*)workspace;
+    a.R = R;
+    a.rows_per_block = plan.rows_per_block;
+    a.H = (int32_t)H;
+    a.nchunk = (int32_t)(H / elems_per_chunk(d->dtype));
+    a.norm = d->norm;
+    a.nacc = plan.nacc;
+    a.scale = (float)(1.0 / (1.0 - (double)d->p));
+    a.inv_h = (float)(1.0 / (double)H);
+
+    if (plan.layout < 0) return SP_ESHAPE;
+    if (plan.blocks > INT32_MAX) return SP_ESHAPE;
+    (void)hipGetLastError();
+    if (plan.blocks > 0) {
+        const Layout L = kLayouts[plan.layout];
+        const BwdKernel k = kBwd[d->dtype == SP_BF16 ? 1 : 0][dR ? 1 : 0][plan.layout];
+        hipLaunchKernelGGL(k, dim3((unsigned)plan.blocks), dim3(block_of(L.tpr)),
+                           (unsigned)plan.lds_bytes, (hipStream_t)stream, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return record_hip(e);
+    }
+    const int ncols = plan.nacc * (int)H;
+    const unsigned fin_grid = (unsigned)((ncols + kFinCols - 1) / kFinCols);
+    hipLaunchKernelGGL(sp_dgamma_finish_kernel, dim3(fin_grid), dim3(kFinCols * kFinSplit), 0,
+                       (hipStream_t)stream, (const float*)workspace, plan.blocks, (int32_t)H,
+                       (int32_t)plan.nacc, dgamma, dbeta);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? SP_OK : record_hip(e);
+}
