@@ -11,10 +11,11 @@ buffer sets that one pass over them moves more than 1.5 GB, well beyond the
 Timed region: K steps launched by replaying a captured HIP graph (so host
 launch cost does not throttle the GPU), bracketed by synchronize on both sides
 and timed by the host clock.  value = algorithmic bytes of fwd + bwd per step /
-time per step.  A second, event-timed pass launches the same calls eagerly
-behind a GPU spin so the queue runs ahead, and records a HIP event pair around
-every forward and backward on their stream: those give the per-launch
-durations behind "roofline" (forward = the dominant kernel).
+time per step.  A second pass replays forward-only and backward-only graphs
+over all buffer sets between HIP event pairs recorded on the kernels' stream:
+the elapsed time divided by the launches gives the per-launch durations behind
+"roofline" (forward = the dominant kernel).  A 1 GiB device copy on the same
+stream is timed as an achievable-bandwidth reference.
 
 cpu_baseline: the CPU oracle, single-threaded, on a bounded sample of the same
 shard's rows (about 10 s of work), with a parity check of those rows against
@@ -137,6 +138,12 @@ def cpu_baseline(sp, w, j, src, outs, seconds):
     t_probe, _, _ = run(probe)
     n = int(max(1, min(w.R, probe * seconds / max(t_probe, 1e-6))))
     t, o, ob = run(n)
+    reps = 1
+    while t * (reps + 1) / reps < seconds and reps < 1000:  # whole shard is quick: repeat it
+        dt, _, _ = run(n)
+        t += dt
+        reps += 1
+    t /= reps
     # algorithmic bytes of the sample (per-row share of the shard's bytes, plus the [H] vectors)
     fwd_b, bwd_b = sp.sp_region_traffic_bytes(sp.make_desc(w.S, w.B, w.H, w.T, j, w.dtype, w.norm))
     per_row = (fwd_b + bwd_b) / w.R
@@ -164,7 +171,7 @@ def cpu_baseline(sp, w, j, src, outs, seconds):
         "cores": 1,
         "kind": "oracle",
         "sample": f"forward + backward of rows 0..{n - 1} of shard {j} ({n} of {w.R} token rows, "
-                  f"{sample_bytes / 1e6:.1f} MB algorithmic) in {t:.2f} s",
+                  f"{sample_bytes / 1e6:.1f} MB algorithmic), {reps} run(s), {t:.3f} s each",
         "tokens_per_s": round(n / t, 2),
         "cpu": _cpu_model(),
         "parity_vs_gpu_sample": "pass" if parity else "FAIL",
@@ -226,32 +233,43 @@ def main():
             step(s)
     torch.cuda.synchronize()
 
-    # graphs: one pass over all sets, and one for the remainder of K
+    # graphs: one pass over all sets, one for the remainder of K, and forward-only
+    # / backward-only passes for the per-launch durations
     K, Wm = args.steps, args.warmup
     reps, rem = divmod(K, n_sets)
-    g_all = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_all, stream=stream):
-        for s in sets:
-            step(s)
-    g_rem = None
-    if rem:
-        g_rem = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g_rem, stream=stream):
-            for s in sets[:rem]:
-                step(s)
+
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            fn()
+        return g
+
+    g_all = capture(lambda: [step(s) for s in sets])
+    g_rem = capture(lambda: [step(s) for s in sets[:rem]]) if rem else None
+    g_fwd = capture(lambda: [s.fwd() for s in sets])
+    g_bwd = capture(lambda: [s.bwd() for s in sets])
     torch.cuda.synchronize()
     # graph replays must reproduce the eager results bit for bit
-    ref = {k: getattr(sets[0], k).clone() for k in ("h", "y", "mask", "rstd", "dres", "dP", "dgamma")}
-    for s in sets:
-        for k in ("h", "y", "dres", "dP"):
-            getattr(s, k).zero_()
-    g_all.replay()
-    torch.cuda.synchronize()
-    graph_ok = all(torch.equal(ref[k], getattr(sets[0], k)) for k in ref)
+    keys = ("h", "y", "mask", "rstd", "dres", "dP", "dgamma")
+    ref = {k: getattr(sets[0], k).clone() for k in keys}
+    graph_ok = True
+    for _ in range(2):
+        for s in sets:
+            for k in ("h", "y", "dres", "dP"):
+                getattr(s, k).zero_()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            g_all.replay()
+        torch.cuda.synchronize()
+        graph_ok = graph_ok and all(torch.equal(ref[k], getattr(sets[0], k)) for k in keys)
+
+    def replay(g, times=1):
+        with torch.cuda.stream(stream):
+            for _ in range(times):
+                g.replay()
 
     # warmup
-    for _ in range(max(1, math.ceil(Wm / n_sets))):
-        g_all.replay()
+    replay(g_all, max(1, math.ceil(Wm / n_sets)))
     torch.cuda.synchronize()
 
     # ---- timed region: exactly K steps ----
@@ -259,39 +277,51 @@ def main():
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(reps):
-        g_all.replay()
-    if g_rem is not None:
-        g_rem.replay()
-    ev1.record(stream)
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        for _ in range(reps):
+            g_all.replay()
+        if g_rem is not None:
+            g_rem.replay()
+        ev1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall_ms = (t1 - t0) * 1e3
     gpu_ms = ev0.elapsed_time(ev1)
     ms_per_step = wall_ms / K
 
-    # ---- per-launch durations: HIP events around each launch on its stream ----
-    n_ev = min(K, 50 * n_sets, 2000)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_ev)]
+    # ---- per-launch durations: HIP events on the kernels' stream around
+    # back-to-back forward launches (one per buffer set), then backward launches
+    ev_reps = max(4, min(50, math.ceil(2000 / n_sets)))
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(ev_reps)]
     torch.cuda.synchronize()
-    h0 = time.perf_counter()
     with torch.cuda.stream(stream):
-        torch.cuda._sleep(50_000_000)  # hold the stream while the host enqueues
-        for i in range(n_ev):
-            s = sets[i % n_sets]
-            evs[i][0].record(stream)
-            s.fwd()
-            evs[i][1].record(stream)
-            s.bwd()
-            evs[i][2].record(stream)
-    enqueue_ms = (time.perf_counter() - h0) * 1e3
+        for m in marks:
+            m[0].record(stream)
+            g_fwd.replay()
+            m[1].record(stream)
+            g_bwd.replay()
+            m[2].record(stream)
     torch.cuda.synchronize()
-    spin_ms = (time.perf_counter() - h0) * 1e3
-    fwd_us = sorted(evs[i][0].elapsed_time(evs[i][1]) * 1e3 for i in range(n_ev))
-    bwd_us = sorted(evs[i][1].elapsed_time(evs[i][2]) * 1e3 for i in range(n_ev))
-    fwd_avg = sum(fwd_us) / n_ev
-    bwd_avg = sum(bwd_us) / n_ev
+    fwd_us = sorted(m[0].elapsed_time(m[1]) * 1e3 / n_sets for m in marks)
+    bwd_us = sorted(m[1].elapsed_time(m[2]) * 1e3 / n_sets for m in marks)
+    fwd_avg = sum(fwd_us) / ev_reps
+    bwd_avg = sum(bwd_us) / ev_reps
+
+    # ---- reference: a plain device-to-device copy of 1 GiB, same stream ----
+    a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    with torch.cuda.stream(stream):
+        b.copy_(a)
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        for _ in range(10):
+            b.copy_(a)
+        c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * a.numel() * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del a, b
 
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = fwd_bytes / (fwd_avg * 1e-6) / 1e9
@@ -318,10 +348,10 @@ def main():
         "bwd_bytes": bwd_bytes,
         "buffer_sets": n_sets,
         "timing": {"method": "hip graph replay, host clock", "gpu_event_ms_per_step": round(gpu_ms / K, 6),
-                   "fwd_us_avg": round(fwd_avg, 3), "fwd_us_median": round(fwd_us[n_ev // 2], 3),
-                   "bwd_us_avg": round(bwd_avg, 3), "bwd_us_median": round(bwd_us[n_ev // 2], 3),
-                   "event_launches": n_ev, "event_pass_enqueue_ms": round(enqueue_ms, 3),
-                   "event_pass_total_ms": round(spin_ms, 3), "graph_replay_matches_eager": graph_ok},
+                   "fwd_us_avg": round(fwd_avg, 3), "fwd_us_median": round(fwd_us[ev_reps // 2], 3),
+                   "bwd_us_avg": round(bwd_avg, 3), "bwd_us_median": round(bwd_us[ev_reps // 2], 3),
+                   "event_launches_each": ev_reps * n_sets, "graph_replay_matches_eager": graph_ok},
+        "copy_reference_GBs": round(copy_gbs, 1),
         "roofline": {
             "kernel": "sp_fwd_kernel",
             "bound": "hbm",

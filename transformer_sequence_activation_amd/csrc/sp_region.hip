@@ -92,11 +92,28 @@ struct Act<SP_F32> {
     }
 };
 
+// Streaming 16-byte accesses: every activation byte is touched once per launch.
+#ifndef SP_NT_LOADS
+#define SP_NT_LOADS 1
+#endif
+#ifndef SP_NT_STORES
+#define SP_NT_STORES 1
+#endif
 __device__ __forceinline__ u32x4 ld16(const void* base, int64_t byte_off) {
-    return *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(base) + byte_off);
+    const u32x4* p = reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(base) + byte_off);
+#if SP_NT_LOADS
+    return __builtin_nontemporal_load(p);
+#else
+    return *p;
+#endif
 }
 __device__ __forceinline__ void st16(void* base, int64_t byte_off, u32x4 v) {
-    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(base) + byte_off) = v;
+    u32x4* p = reinterpret_cast<u32x4*>(reinterpret_cast<char*>(base) + byte_off);
+#if SP_NT_STORES
+    __builtin_nontemporal_store(v, p);
+#else
+    *p = v;
+#endif
 }
 
 // ---------------------------------------------------------------------------
@@ -626,33 +643,49 @@ __global__ __launch_bounds__(BLOCK) void sp_bwd_kernel(const BwdArgs a) {
 }
 
 // dgamma[k] (and dbeta[k]) = sum over the G workgroup partials, in a fixed
-// order: four lanes split the partials into contiguous quarters and the
-// quarters are added in order.
-constexpr int kFinCols = 64;
-constexpr int kFinSplit = 4;
+// order.  A block covers kFinGroups groups of four adjacent columns (one 16-byte
+// load each) and splits the G partial rows into kFinSlices contiguous slices, one
+// per lane; a lane issues all of its slice's loads before adding them in order,
+// then the slices are added in order through LDS.
+#ifndef SP_FIN_SLICES
+#define SP_FIN_SLICES 32
+#endif
+constexpr int kFinGroups = 16;
+constexpr int kFinSlices = SP_FIN_SLICES;
+constexpr int kFinBatch = 8;
 
-__global__ __launch_bounds__(kFinCols* kFinSplit) void sp_dgamma_finish_kernel(
+__global__ __launch_bounds__(kFinGroups* kFinSlices) void sp_dgamma_finish_kernel(
     const float* ws, int64_t G, int32_t H, int32_t nacc, float* dgamma, float* dbeta) {
-    __shared__ float part[kFinSplit][kFinCols];
-    const int n = nacc * H;
-    const int ci = threadIdx.x % kFinCols;
-    const int sp = threadIdx.x / kFinCols;
-    const int c = blockIdx.x * kFinCols + ci;
-    const int64_t per = (G + kFinSplit - 1) / kFinSplit;
-    const int64_t g0 = sp * per;
+    __shared__ f32x4 part[kFinSlices][kFinGroups];
+    const int n = nacc * H;  // a multiple of 4
+    const int cg = threadIdx.x % kFinGroups;
+    const int sl = threadIdx.x / kFinGroups;
+    const int c = (blockIdx.x * kFinGroups + cg) * 4;
+    const int64_t per = (G + kFinSlices - 1) / kFinSlices;
+    const int64_t g0 = sl * per;
     const int64_t g1 = min(g0 + per, G);
-    float v = 0.0f;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
     if (c < n) {
-        for (int64_t g = g0; g < g1; ++g) v += ws[g * n + c];
-    }
-    part[sp][ci] = v;
-    __syncthreads();
-    if (sp == 0 && c < n) {
-        float s = part[0][ci];
+        const float* src = ws + c;
+        int64_t g = g0;
+        for (; g + kFinBatch <= g1; g += kFinBatch) {
+            f32x4 v[kFinBatch];
 #pragma unroll
-        for (int q = 1; q < kFinSplit; ++q) s += part[q][ci];
-        if (c < H) dgamma[c] = s;
-        else dbeta[c - H] = s;
+            for (int b = 0; b < kFinBatch; ++b)
+                v[b] = *reinterpret_cast<const f32x4*>(src + (g + b) * n);
+#pragma unroll
+            for (int b = 0; b < kFinBatch; ++b) acc += v[b];
+        }
+        for (; g < g1; ++g) acc += *reinterpret_cast<const f32x4*>(src + g * n);
+    }
+    part[sl][cg] = acc;
+    __syncthreads();
+    if (sl == 0 && c < n) {
+        f32x4 s = part[0][cg];
+#pragma unroll
+        for (int q = 1; q < kFinSlices; ++q) s += part[q][cg];
+        float* dst = c < H ? dgamma + c : dbeta + (c - H);
+        *reinterpret_cast<f32x4*>(dst) = s;
     }
 }
 
@@ -660,16 +693,27 @@ __global__ __launch_bounds__(kFinCols* kFinSplit) void sp_dgamma_finish_kernel(
 // Launch layouts: (lanes per row, chunks per lane) by row length in chunks.
 
 struct Layout {
-    int tpr, cpt, max_chunks;
+    int tpr, cpt;
 };
+// Entries 0..kNumDefault-1 are the default choices, in increasing capacity
+// (tpr * cpt chunks); the rest are alternatives kept for tuning.
 constexpr Layout kLayouts[] = {
-    {16, 1, 16},   {32, 1, 32},   {64, 1, 64},  {32, 3, 96},   {64, 2, 128},   {64, 3, 192},
-    {64, 4, 256},  {512, 1, 512}, {512, 2, 1024}, {512, 4, 2048}, {1024, 4, 4096}, {1024, 8, 8192},
+    {16, 1},  {32, 1},  {64, 1},  {32, 3},   {64, 2},    {64, 3},  {64, 4},  {512, 1},  {512, 2},
+    {512, 4}, {1024, 4}, {1024, 8}, {128, 4}, {256, 2},  {256, 4}, {1024, 1}, {128, 8},
 };
 constexpr int kNumLayouts = sizeof(kLayouts) / sizeof(kLayouts[0]);
+constexpr int kNumDefault = 12;
 constexpr int kSubWaveBlock = 256;  // block size of the layouts whose rows fit in one wavefront
 
 constexpr int block_of(int tpr) { return tpr <= kWave ? kSubWaveBlock : tpr; }
+
+// Compile-time overrides (layout indices) used when tuning; -1 = default choice.
+#ifndef SP_FWD_LAYOUT
+#define SP_FWD_LAYOUT -1
+#endif
+#ifndef SP_BWD_LAYOUT
+#define SP_BWD_LAYOUT -1
+#endif
 
 typedef void (*FwdKernel)(FwdArgs);
 typedef void (*BwdKernel)(BwdArgs);
@@ -678,7 +722,8 @@ typedef void (*BwdKernel)(BwdArgs);
     X(16, 1, __VA_ARGS__), X(32, 1, __VA_ARGS__), X(64, 1, __VA_ARGS__), X(32, 3, __VA_ARGS__),   \
         X(64, 2, __VA_ARGS__), X(64, 3, __VA_ARGS__), X(64, 4, __VA_ARGS__),                      \
         X(512, 1, __VA_ARGS__), X(512, 2, __VA_ARGS__), X(512, 4, __VA_ARGS__),                   \
-        X(1024, 4, __VA_ARGS__), X(1024, 8, __VA_ARGS__)
+        X(1024, 4, __VA_ARGS__), X(1024, 8, __VA_ARGS__), X(128, 4, __VA_ARGS__),                 \
+        X(256, 2, __VA_ARGS__), X(256, 4, __VA_ARGS__), X(1024, 1, __VA_ARGS__), X(128, 8, __VA_ARGS__)
 
 #define SP_FWD_ENTRY(TPR, CPT, DT, TT) &sp_fwd_kernel<DT, TT, TPR, CPT, block_of(TPR)>
 #define SP_BWD_ENTRY(TPR, CPT, DT, HDR) &sp_bwd_kernel<DT, TPR, CPT, block_of(TPR), HDR>
@@ -743,9 +788,12 @@ bool any_overlap(const Span* outs, int nout, const Span* ins, int nin) {
     return false;
 }
 
-int pick_layout(int64_t nchunk) {
-    for (int i = 0; i < kNumLayouts; ++i)
-        if (nchunk <= kLayouts[i].max_chunks) return i;
+int capacity(int li) { return kLayouts[li].tpr * kLayouts[li].cpt; }
+
+int pick_layout(int64_t nchunk, int forced) {
+    if (forced >= 0 && forced < kNumLayouts && nchunk <= capacity(forced)) return forced;
+    for (int i = 0; i < kNumDefault; ++i)
+        if (nchunk <= capacity(i)) return i;
     return -1;
 }
 
@@ -772,7 +820,8 @@ BwdPlan plan_bwd(const sp_desc_t* d) {
     BwdPlan p{};
     const int64_t R = shard_rows(d);
     const int64_t nchunk = d->H / elems_per_chunk(d->dtype);
-    p.layout = pick_layout(nchunk);
+    p.layout = pick_layout(nchunk, SP_BWD_LAYOUT);
+    if (p.layout < 0) return p;  // unreachable for a validated descriptor
     const int tpr = kLayouts[p.layout].tpr;
     const int rpw = block_of(tpr) / tpr;
     p.nacc = d->norm == SP_LAYERNORM ? 2 : 1;
@@ -900,7 +949,7 @@ extern "C" int sp_region_fwd(const sp_desc_t* d, const void* const* P, const voi
     a.eps = d->eps;
     a.inv_h = (float)(1.0 / (double)H);
 
-    const int li = pick_layout(a.nchunk);
+    const int li = pick_layout(a.nchunk, SP_FWD_LAYOUT);
     if (li < 0) return SP_ESHAPE;
     const Layout L = kLayouts[li];
     const int block = block_of(L.tpr);
@@ -989,8 +1038,8 @@ extern "C" int sp_region_bwd(const sp_desc_t* d, const void* dY, const void* h, 
         if (e != hipSuccess) return record_hip(e);
     }
     const int ncols = plan.nacc * (int)H;
-    const unsigned fin_grid = (unsigned)((ncols + kFinCols - 1) / kFinCols);
-    hipLaunchKernelGGL(sp_dgamma_finish_kernel, dim3(fin_grid), dim3(kFinCols * kFinSplit), 0,
+    const unsigned fin_grid = (unsigned)((ncols / 4 + kFinGroups - 1) / kFinGroups);
+    hipLaunchKernelGGL(sp_dgamma_finish_kernel, dim3(fin_grid), dim3(kFinGroups * kFinSlices), 0,
                        (hipStream_t)stream, (const float*)workspace, plan.blocks, (int32_t)H,
                        (int32_t)plan.nacc, dgamma, dbeta);
     const hipError_t e = hipGetLastError();
