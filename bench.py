@@ -1,25 +1,27 @@
-"""Benchmark of the SP-region forward + backward on one shard, one MI355X.
+"""Benchmark of the SP-region forward + backward, one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
 
-A step is one pass of the whole path over one shard: sp_region_fwd then
-sp_region_bwd (its main kernel and the dgamma finish).  Inputs are seeded
-synthetic tensors already resident in HBM.  Steps rotate over enough disjoint
-buffer sets that one pass over them moves more than 1.5 GB, well beyond the
-256 MB Infinity Cache, so every step reads HBM.
+A step is one pass of the whole path over one batch: sp_region_fwd then
+sp_region_bwd (its main kernel and the dgamma finish) on one shard -- or, for
+the long-sequence workload, on all of its shards one after another.  Inputs are
+seeded synthetic tensors already resident in HBM.  Steps rotate over enough
+disjoint buffer sets that one pass over them moves more than 1.5 GB, well beyond
+the 256 MB Infinity Cache, so every step reads HBM.
 
-Timed region: K steps launched by replaying a captured HIP graph (so host
-launch cost does not throttle the GPU), bracketed by synchronize on both sides
-and timed by the host clock.  value = algorithmic bytes of fwd + bwd per step /
-time per step.  A second pass replays forward-only and backward-only graphs
-over all buffer sets between HIP event pairs recorded on the kernels' stream:
-the elapsed time divided by the launches gives the per-launch durations behind
-"roofline" (forward = the dominant kernel).  A 1 GiB device copy on the same
-stream is timed as an achievable-bandwidth reference.
+Timed region: K steps launched by replaying captured HIP graphs (so host launch
+cost does not throttle the GPU), bracketed by synchronize on both sides and
+timed by the host clock.  value = algorithmic bytes of fwd + bwd per step / time
+per step.  A second pass replays forward-only and backward-only graphs over all
+buffer sets between HIP event pairs recorded on the kernels' stream: elapsed
+time / launches gives the per-launch durations behind "roofline" (the forward is
+the dominant kernel).  A 1 GiB device copy on the same stream is timed as an
+achievable-bandwidth reference.  The other workloads are measured the same way
+with fewer steps and reported under "workloads".
 
-cpu_baseline: the CPU oracle, single-threaded, on a bounded sample of the same
-shard's rows (about 10 s of work), with a parity check of those rows against
-the GPU's outputs.
+cpu_baseline: the CPU oracle, single-threaded, on a bounded sample of the
+headline shard (about 10 s of work), with a parity check of that sample
+against the GPU's outputs.
 """
 import argparse
 import hashlib
@@ -33,6 +35,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 DEFAULT_WORKLOAD = "layernorm_T8_S4096_B1_H4096"
+SECONDARY = ["minimind_T2_S2048_B2_H768", "large_hidden_T8_S8192_B2_H8192",
+             "long_seq_T8_S32768_B1_H8192"]
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
 ROTATE_BYTES = 1.5e9
 PROFILES = os.path.join(ROOT, "profiles")
@@ -44,9 +48,13 @@ def parse():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--shard", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--profile-pass", action="store_true",
+                    help="no timing: run a few eager forward/backward launches on cold buffer sets "
+                         "and a 256 MiB device copy (the reference for hardware byte counters), "
+                         "for use under rocprofv3")
     return ap.parse_args()
 
 
@@ -70,20 +78,19 @@ def load_traffic(workload):
     return rec
 
 
-class SetBuffers:
-    """One disjoint set of inputs and outputs for one step."""
+class ShardBuffers:
+    """Per-shard inputs and outputs of one buffer set."""
 
-    def __init__(self, sp, w, j, src):
+    def __init__(self, sp, w, j, src, P):
         import torch
-        dev = "cuda"
-        act = w.torch_dtype
-        R, H = w.R, w.H
-        self.P = [p.clone() for p in src["P"]]
-        self.res = src["res"].clone()
-        self.dY = src["dY"].clone()
-        self.gamma = src["gamma"].clone()
-        self.beta = None if src["beta"] is None else src["beta"].clone()
+        dev, act, R, H = "cuda", w.torch_dtype, w.R, w.H
         ln = w.norm == "ln"
+        self.j = j
+        self.P = P
+        self.res = src["res"][j].clone()
+        self.dY = src["dY"][j].clone()
+        self.gamma = src["gamma"]
+        self.beta = src["beta"]
         self.h = torch.empty((R, H), dtype=act, device=dev)
         self.y = torch.empty((R, H), dtype=act, device=dev)
         self.mask = torch.empty((R, H), dtype=torch.uint8, device=dev)
@@ -93,9 +100,8 @@ class SetBuffers:
         self.dP = torch.empty((R, H), dtype=act, device=dev)
         self.dgamma = torch.empty(H, device=dev)
         self.dbeta = torch.empty(H, device=dev) if ln else None
-        d = sp.make_desc(w.S, w.B, w.H, w.T, j, w.dtype, w.norm, w.eps, w.p, w.seed)
-        self.desc = d
-        self.ws_bytes = max(16, sp.sp_region_bwd_workspace_size(d))
+        self.desc = sp.make_desc(w.S, w.B, w.H, w.T, j, w.dtype, w.norm, w.eps, w.p, w.seed)
+        self.ws_bytes = max(16, sp.sp_region_bwd_workspace_size(self.desc))
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
 
     def prepare(self, sp, stream):
@@ -104,6 +110,162 @@ class SetBuffers:
         self.bwd = sp.prepare_bwd(self.desc, self.dY, self.h, self.mask, self.mean, self.rstd,
                                   self.gamma, None, self.dres, self.dP, self.dgamma, self.dbeta,
                                   self.ws, self.ws_bytes, stream=stream)
+
+
+class BufferSet:
+    """One disjoint set: its own copy of the full partial buffers and the shards' tensors."""
+
+    def __init__(self, sp, w, shards, src):
+        self.P = [p.clone() for p in src["P"]]
+        self.shards = [ShardBuffers(sp, w, j, src, self.P) for j in shards]
+
+    def prepare(self, sp, stream):
+        for s in self.shards:
+            s.prepare(sp, stream)
+
+    def step(self):
+        for s in self.shards:
+            s.fwd()
+            s.bwd()
+
+
+def make_source(w, shards):
+    """Seeded inputs on the GPU: full partials, per-shard residual / dY slices."""
+    from transformer_sequence_activation_amd import workloads as W
+    res = W.residual(w, "cuda")
+    dY = W.grad_y(w, "cuda")
+    src = {
+        "P": [W.partial(w, t, "cuda") for t in range(w.T)],
+        "res": {j: W.shard(res, w, j).clone() for j in shards},
+        "dY": {j: W.shard(dY, w, j).clone() for j in shards},
+        "gamma": W.gamma(w, "cuda"),
+        "beta": W.beta(w, "cuda"),
+    }
+    del res, dY
+    return src
+
+
+def measure(sp, w, shards, K, Wm, stream):
+    """Time K steps (graph replay, host clock) and per-launch durations (events)."""
+    import torch
+
+    src = make_source(w, shards)
+    fwd_b = bwd_b = 0
+    for j in shards:
+        f, b = sp.sp_region_traffic_bytes(sp.make_desc(w.S, w.B, w.H, w.T, j, w.dtype, w.norm))
+        fwd_b += f
+        bwd_b += b
+    step_bytes = fwd_b + bwd_b
+    n_sets = max(2, math.ceil(ROTATE_BYTES / step_bytes))
+    n_sets = min(n_sets, max(2, K))
+    sets = [BufferSet(sp, w, shards, src) for _ in range(n_sets)]
+    for s in sets:
+        s.prepare(sp, stream.cuda_stream)
+    torch.cuda.synchronize()  # the copies above ran on torch's current stream, not on `stream`
+    with torch.cuda.stream(stream):
+        for s in sets:
+            s.step()
+    torch.cuda.synchronize()
+
+    reps, rem = divmod(K, n_sets)
+
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            fn()
+        return g
+
+    g_all = capture(lambda: [s.step() for s in sets])
+    g_rem = capture(lambda: [s.step() for s in sets[:rem]]) if rem else None
+    g_fwd = capture(lambda: [sh.fwd() for s in sets for sh in s.shards])
+    g_bwd = capture(lambda: [sh.bwd() for s in sets for sh in s.shards])
+    torch.cuda.synchronize()
+
+    # graph replays must reproduce the eager results bit for bit
+    keys = ("h", "y", "mask", "rstd", "dres", "dP", "dgamma")
+    first = sets[0].shards[0]
+    ref = {k: getattr(first, k).clone() for k in keys}
+    graph_bad = set()
+    for _ in range(2):
+        for s in sets:
+            for sh in s.shards:
+                for k in ("h", "y", "dres", "dP", "dgamma"):
+                    getattr(sh, k).zero_()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            g_all.replay()
+        torch.cuda.synchronize()
+        graph_bad |= {k for k in keys if not torch.equal(ref[k], getattr(first, k))}
+    graph_ok = not graph_bad
+
+    with torch.cuda.stream(stream):
+        for _ in range(max(1, math.ceil(Wm / n_sets))):
+            g_all.replay()
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps ----
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        for _ in range(reps):
+            g_all.replay()
+        if g_rem is not None:
+            g_rem.replay()
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+    gpu_ms_per_step = ev0.elapsed_time(ev1) / K
+
+    # ---- per-launch durations: HIP events on the kernels' stream around
+    # back-to-back forward launches (one per buffer set and shard), then backward
+    launches = n_sets * len(shards)
+    ev_reps = max(4, min(50, math.ceil(2000 / launches)))
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(ev_reps)]
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for m in marks:
+            m[0].record(stream)
+            g_fwd.replay()
+            m[1].record(stream)
+            g_bwd.replay()
+            m[2].record(stream)
+    torch.cuda.synchronize()
+    fwd_us = sorted(m[0].elapsed_time(m[1]) * 1e3 / launches for m in marks)
+    bwd_us = sorted(m[1].elapsed_time(m[2]) * 1e3 / launches for m in marks)
+    out = {
+        "workload": w.name, "shards": list(shards), "steps": K,
+        "ms_per_step": ms_per_step, "gpu_event_ms_per_step": gpu_ms_per_step,
+        "value_GBs": step_bytes / (ms_per_step * 1e-3) / 1e9,
+        "tokens_per_s": w.R * len(shards) / (ms_per_step * 1e-3),
+        "bytes_per_step": step_bytes, "fwd_bytes": fwd_b // len(shards), "bwd_bytes": bwd_b // len(shards),
+        "buffer_sets": n_sets,
+        "fwd_us_avg": sum(fwd_us) / ev_reps, "fwd_us_median": fwd_us[ev_reps // 2],
+        "bwd_us_avg": sum(bwd_us) / ev_reps, "bwd_us_median": bwd_us[ev_reps // 2],
+        "event_launches_each": ev_reps * launches,
+        "graph_replay_matches_eager": graph_ok,
+        "graph_replay_mismatch": sorted(graph_bad),
+    }
+    return out, src, sets
+
+
+def copy_reference(stream):
+    import torch
+    a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    with torch.cuda.stream(stream):
+        b.copy_(a)
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        for _ in range(10):
+            b.copy_(a)
+        c1.record(stream)
+    torch.cuda.synchronize()
+    return 2 * a.numel() * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
 
 
 def cpu_baseline(sp, w, j, src, outs, seconds):
@@ -125,8 +287,8 @@ def cpu_baseline(sp, w, j, src, outs, seconds):
 
     def run(n):
         P = [u16(W.shard(p, w, j)[:n]) for p in src["P"]]  # full partials: slice shard j
-        res = u16(src["res"][:n])                           # already the shard
-        dY = u16(src["dY"][:n])
+        res = u16(src["res"][j][:n])
+        dY = u16(src["dY"][j][:n])
         t0 = time.perf_counter()
         o = oracle.fwd(od, P, res, gam, bet, row0=0, nrows=n)
         ob = oracle.bwd(od, dY, o["h"], o["mask"],
@@ -139,16 +301,13 @@ def cpu_baseline(sp, w, j, src, outs, seconds):
     n = int(max(1, min(w.R, probe * seconds / max(t_probe, 1e-6))))
     t, o, ob = run(n)
     reps = 1
-    while t * (reps + 1) / reps < seconds and reps < 1000:  # whole shard is quick: repeat it
+    while t * (reps + 1) / reps < seconds and reps < 1000:  # the whole shard is quick: repeat it
         dt, _, _ = run(n)
         t += dt
         reps += 1
     t /= reps
-    # algorithmic bytes of the sample (per-row share of the shard's bytes, plus the [H] vectors)
     fwd_b, bwd_b = sp.sp_region_traffic_bytes(sp.make_desc(w.S, w.B, w.H, w.T, j, w.dtype, w.norm))
-    per_row = (fwd_b + bwd_b) / w.R
-    sample_bytes = per_row * n
-    # parity of the sample against the GPU's first set
+    sample_bytes = (fwd_b + bwd_b) / w.R * n
     mask_ok = bool(np.array_equal(outs.mask[:n].cpu().numpy(), o["mask"]))
     h_ok = bool(np.array_equal(u16(outs.h[:n]), o["h"]))
     bf = oracle.bf16_to_f32 if w.dtype == "bf16" else (lambda a: a)
@@ -160,11 +319,11 @@ def cpu_baseline(sp, w, j, src, outs, seconds):
         return bool(np.all(np.abs(g - r) <= rtol * np.abs(r) + rtol * rms))
 
     rt = 1e-2 if w.dtype == "bf16" else 1e-5
-    y_ok = within(bf(u16(outs.y[:n])), bf(o["y"]), rt)
-    dres_ok = within(bf(u16(outs.dres[:n])), bf(ob["d_res"]), rt)
-    dp_ok = within(bf(u16(outs.dP[:n])), bf(ob["dP"]), rt)
-    rstd_ok = within(outs.rstd[:n].cpu().numpy(), o["rstd"], 1e-5)
-    parity = all([mask_ok, h_ok, y_ok, dres_ok, dp_ok, rstd_ok])
+    parity = all([mask_ok, h_ok,
+                  within(bf(u16(outs.y[:n])), bf(o["y"]), rt),
+                  within(bf(u16(outs.dres[:n])), bf(ob["d_res"]), rt),
+                  within(bf(u16(outs.dP[:n])), bf(ob["dP"]), rt),
+                  within(outs.rstd[:n].cpu().numpy(), o["rstd"], 1e-5)])
     return {
         "value": round(sample_bytes / t / 1e9, 4),
         "unit": "GB/s",
@@ -189,12 +348,35 @@ def _cpu_model():
     return "unknown"
 
 
+def profile_pass(sp, w, stream):
+    """Eager launches for rocprofv3: a 256 MiB copy, then every set three times."""
+    import torch
+    shards = (w.shards[0],)
+    src = make_source(w, shards)
+    f, b = sp.sp_region_traffic_bytes(sp.make_desc(w.S, w.B, w.H, w.T, shards[0], w.dtype, w.norm))
+    n_sets = max(2, math.ceil(ROTATE_BYTES / (f + b)))
+    sets = [BufferSet(sp, w, shards, src) for _ in range(n_sets)]
+    for s in sets:
+        s.prepare(sp, stream.cuda_stream)
+    a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    c = torch.empty_like(a)
+    torch.cuda.synchronize()  # buffer copies ran on torch's current stream
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            c.copy_(a)
+        for _ in range(3):
+            for s in sets:
+                s.step()
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_pass": w.name, "shard": shards[0], "buffer_sets": n_sets,
+                      "copy_bytes": a.numel(), "fwd_bytes": f, "bwd_bytes": b}))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
-              "(the path has no collectives; see the sharding note in the design notes).",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: this build runs one "
+              "rank's shard on one GPU and has no collectives.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -203,137 +385,26 @@ def main():
     from transformer_sequence_activation_amd import workloads as W
 
     sp.load()
-    w = W.WORKLOADS[args.workload]
-    j = w.shards[0] if args.shard is None else args.shard
     torch.cuda.set_device(0)
-    src = {
-        "P": [W.partial(w, t, "cuda") for t in range(w.T)],
-        "res": W.shard(W.residual(w, "cuda"), w, j).clone(),
-        "dY": W.shard(W.grad_y(w, "cuda"), w, j).clone(),
-        "gamma": W.gamma(w, "cuda"),
-        "beta": W.beta(w, "cuda"),
-    }
-    d0 = sp.make_desc(w.S, w.B, w.H, w.T, j, w.dtype, w.norm, w.eps, w.p, w.seed)
-    fwd_bytes, bwd_bytes = sp.sp_region_traffic_bytes(d0)
-    step_bytes = fwd_bytes + bwd_bytes
-    n_sets = max(2, math.ceil(ROTATE_BYTES / step_bytes))
-    n_sets = min(n_sets, args.steps) if args.steps >= 2 else n_sets
     stream = torch.cuda.Stream()
-    sets = [SetBuffers(sp, w, j, src) for _ in range(n_sets)]
-    for s in sets:
-        s.prepare(sp, stream.cuda_stream)
+    w = W.WORKLOADS[args.workload]
+    if args.profile_pass:
+        profile_pass(sp, w, stream)
+        return
 
-    def step(s):
-        s.fwd()
-        s.bwd()
-
-    # eager run on every set (also the warm start of the allocator and code objects)
-    with torch.cuda.stream(stream):
-        for s in sets:
-            step(s)
-    torch.cuda.synchronize()
-
-    # graphs: one pass over all sets, one for the remainder of K, and forward-only
-    # / backward-only passes for the per-launch durations
-    K, Wm = args.steps, args.warmup
-    reps, rem = divmod(K, n_sets)
-
-    def capture(fn):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            fn()
-        return g
-
-    g_all = capture(lambda: [step(s) for s in sets])
-    g_rem = capture(lambda: [step(s) for s in sets[:rem]]) if rem else None
-    g_fwd = capture(lambda: [s.fwd() for s in sets])
-    g_bwd = capture(lambda: [s.bwd() for s in sets])
-    torch.cuda.synchronize()
-    # graph replays must reproduce the eager results bit for bit
-    keys = ("h", "y", "mask", "rstd", "dres", "dP", "dgamma")
-    ref = {k: getattr(sets[0], k).clone() for k in keys}
-    graph_ok = True
-    for _ in range(2):
-        for s in sets:
-            for k in ("h", "y", "dres", "dP"):
-                getattr(s, k).zero_()
-        torch.cuda.synchronize()
-        with torch.cuda.stream(stream):
-            g_all.replay()
-        torch.cuda.synchronize()
-        graph_ok = graph_ok and all(torch.equal(ref[k], getattr(sets[0], k)) for k in keys)
-
-    def replay(g, times=1):
-        with torch.cuda.stream(stream):
-            for _ in range(times):
-                g.replay()
-
-    # warmup
-    replay(g_all, max(1, math.ceil(Wm / n_sets)))
-    torch.cuda.synchronize()
-
-    # ---- timed region: exactly K steps ----
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    with torch.cuda.stream(stream):
-        ev0.record(stream)
-        for _ in range(reps):
-            g_all.replay()
-        if g_rem is not None:
-            g_rem.replay()
-        ev1.record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    wall_ms = (t1 - t0) * 1e3
-    gpu_ms = ev0.elapsed_time(ev1)
-    ms_per_step = wall_ms / K
-
-    # ---- per-launch durations: HIP events on the kernels' stream around
-    # back-to-back forward launches (one per buffer set), then backward launches
-    ev_reps = max(4, min(50, math.ceil(2000 / n_sets)))
-    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(ev_reps)]
-    torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        for m in marks:
-            m[0].record(stream)
-            g_fwd.replay()
-            m[1].record(stream)
-            g_bwd.replay()
-            m[2].record(stream)
-    torch.cuda.synchronize()
-    fwd_us = sorted(m[0].elapsed_time(m[1]) * 1e3 / n_sets for m in marks)
-    bwd_us = sorted(m[1].elapsed_time(m[2]) * 1e3 / n_sets for m in marks)
-    fwd_avg = sum(fwd_us) / ev_reps
-    bwd_avg = sum(bwd_us) / ev_reps
-
-    # ---- reference: a plain device-to-device copy of 1 GiB, same stream ----
-    a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-    b = torch.empty_like(a)
-    with torch.cuda.stream(stream):
-        b.copy_(a)
-        c0 = torch.cuda.Event(enable_timing=True)
-        c1 = torch.cuda.Event(enable_timing=True)
-        c0.record(stream)
-        for _ in range(10):
-            b.copy_(a)
-        c1.record(stream)
-    torch.cuda.synchronize()
-    copy_gbs = 2 * a.numel() * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
-    del a, b
-
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    achieved = fwd_bytes / (fwd_avg * 1e-6) / 1e9
+    j = w.shards[0]
+    head, src, sets = measure(sp, w, (j,), args.steps, args.warmup, stream)
+    copy_gbs = copy_reference(stream)
+    achieved = head["fwd_bytes"] / (head["fwd_us_avg"] * 1e-6) / 1e9
     traffic = load_traffic(w.name)
     line = {
         "metric": "achieved HBM GB/s (and % of peak) for SP-region fused fwd+bwd on one shard",
-        "value": round(value, 2),
+        "value": round(head["value_GBs"], 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": K,
-        "warmup": Wm,
-        "ms_per_step": round(ms_per_step, 6),
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -341,16 +412,18 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "S": w.S, "B": w.B, "H": w.H, "shard": j,
                    "norm": w.norm, "p": w.p, "eps": w.eps, "parallelism": "one shard, 1 GPU"},
-        "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
-        "tokens_per_s": round(w.R / (ms_per_step * 1e-3), 1),
-        "bytes_per_step": step_bytes,
-        "fwd_bytes": fwd_bytes,
-        "bwd_bytes": bwd_bytes,
-        "buffer_sets": n_sets,
-        "timing": {"method": "hip graph replay, host clock", "gpu_event_ms_per_step": round(gpu_ms / K, 6),
-                   "fwd_us_avg": round(fwd_avg, 3), "fwd_us_median": round(fwd_us[ev_reps // 2], 3),
-                   "bwd_us_avg": round(bwd_avg, 3), "bwd_us_median": round(bwd_us[ev_reps // 2], 3),
-                   "event_launches_each": ev_reps * n_sets, "graph_replay_matches_eager": graph_ok},
+        "pct_of_peak": round(100 * head["value_GBs"] / PEAK_HBM_GBS, 2),
+        "tokens_per_s": round(head["tokens_per_s"], 1),
+        "bytes_per_step": head["bytes_per_step"],
+        "fwd_bytes": head["fwd_bytes"],
+        "bwd_bytes": head["bwd_bytes"],
+        "buffer_sets": head["buffer_sets"],
+        "timing": {"method": "hip graph replay, host clock",
+                   "gpu_event_ms_per_step": round(head["gpu_event_ms_per_step"], 6),
+                   "fwd_us_avg": round(head["fwd_us_avg"], 3), "fwd_us_median": round(head["fwd_us_median"], 3),
+                   "bwd_us_avg": round(head["bwd_us_avg"], 3), "bwd_us_median": round(head["bwd_us_median"], 3),
+                   "event_launches_each": head["event_launches_each"],
+                   "graph_replay_matches_eager": head["graph_replay_matches_eager"]},
         "copy_reference_GBs": round(copy_gbs, 1),
         "roofline": {
             "kernel": "sp_fwd_kernel",
@@ -362,11 +435,31 @@ def main():
             "traffic": None if traffic is None else traffic["fwd_bytes_per_launch"],
         },
         "cpu_baseline": None,
+        "workloads": {},
     }
     if traffic is not None:
         line["roofline"]["traffic_detail"] = traffic
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(sp, w, j, src, sets[0], args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(sp, w, j, src, sets[0].shards[0], args.cpu_seconds)
+    del src, sets
+    torch.cuda.empty_cache()
+    if not args.no_secondary:
+        for name in SECONDARY:
+            ws = W.WORKLOADS[name]
+            shards = ws.shards if len(ws.shards) > 2 else (ws.shards[0],)
+            K2 = 40 if len(shards) > 2 else 400
+            r, s2, st2 = measure(sp, ws, tuple(shards), K2, max(10, K2 // 10), stream)
+            line["workloads"][name] = {
+                "shards_per_step": len(shards), "steps": K2,
+                "GBs": round(r["value_GBs"], 1), "pct_of_peak": round(100 * r["value_GBs"] / PEAK_HBM_GBS, 2),
+                "ms_per_step": round(r["ms_per_step"], 5), "tokens_per_s": round(r["tokens_per_s"], 1),
+                "fwd_us": round(r["fwd_us_avg"], 2), "bwd_us": round(r["bwd_us_avg"], 2),
+                "fwd_kernel_GBs": round(r["fwd_bytes"] / (r["fwd_us_avg"] * 1e-6) / 1e9, 1),
+                "graph_replay_matches_eager": r["graph_replay_matches_eager"],
+                "graph_replay_mismatch": r["graph_replay_mismatch"],
+            }
+            del s2, st2
+            torch.cuda.empty_cache()
     print(json.dumps(line), flush=True)
 
 

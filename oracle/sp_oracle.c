@@ -25,7 +25,7 @@
  *   RMSNorm casts the bf16 stream to fp32, multiplies by the weight in fp32 and
  *   casts back to the activation type.
  *
- * Readings taken where the pages leave a step open (all listed in the design doc):
+ * Readings taken where the pages leave a step open:
  *   - order: sum of partials -> dropout -> + residual -> norm; outputs are the
  *     residual stream h and the normalised y.
  *   - element-wise arithmetic of the bf16/fp32 modes is fp32 with one rounding

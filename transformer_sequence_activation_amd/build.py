@@ -11,6 +11,8 @@ ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "sp_region.hip")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsp_region.so")
+PROBE_SRC = os.path.join(PKG, "csrc", "stream_probe.hip")
+PROBE = os.path.join(PKG, "stream_probe")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -40,10 +42,26 @@ def build(out=LIB, defines=(), resource_usage=False, verbose=False):
     return out
 
 
+def build_probe(out=PROBE, verbose=False):
+    """Compile the streaming-bandwidth probe executable; always recompiles."""
+    hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
+    flags = [f for f in HIPCC_FLAGS if f not in ("-fPIC", "-shared")]
+    tmp = out + ".tmp"
+    cmd = [hipcc, *flags, PROBE_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--out", default=LIB)
     ap.add_argument("-D", dest="defines", action="append", default=[])
     ap.add_argument("--resource-usage", action="store_true")
+    ap.add_argument("--probe", action="store_true", help="also build the stream_probe executable")
     args = ap.parse_args()
     print(build(args.out, args.defines, args.resource_usage, verbose=True))
+    if args.probe:
+        print(build_probe(verbose=True))

@@ -470,7 +470,8 @@ struct BwdArgs {
     float inv_h;
 };
 
-template <int DT, int CPT, int E>
+// One token row's backward inputs as loaded (packed).
+template <int CPT, int E>
 struct BwdRow {
     u32x4 dy[CPT];
     u32x4 hh[CPT];
@@ -479,9 +480,9 @@ struct BwdRow {
     float mu, rs;
 };
 
-template <int DT, int TPR, int CPT, int BLOCK, bool HAS_DR>
+template <int DT, bool LN, int CPT, bool HAS_DR>
 __device__ __forceinline__ void bwd_load(const BwdArgs& a, int64_t rowc, const int (&col)[CPT],
-                                         BwdRow<DT, CPT, Act<DT>::E>& b) {
+                                         BwdRow<CPT, Act<DT>::E>& b) {
     using A = Act<DT>;
     constexpr int E = A::E;
     constexpr int EB = A::kBytes;
@@ -495,25 +496,45 @@ __device__ __forceinline__ void bwd_load(const BwdArgs& a, int64_t rowc, const i
         b.m[k] = *reinterpret_cast<const typename MaskWord<E>::type*>(a.mask + idx);
     }
     b.rs = a.rstd[rowc];
-    b.mu = (a.norm == SP_LAYERNORM) ? a.mean[rowc] : 0.0f;
+    b.mu = LN ? a.mean[rowc] : 0.0f;
 }
 
-template <int DT, int TPR, int CPT, int BLOCK, bool HAS_DR>
-__global__ __launch_bounds__(BLOCK) void sp_bwd_kernel(const BwdArgs a) {
+// The PF rows one row group takes in step `it` (rows past the tile's end are
+// loaded from a valid row and never stored).
+template <int DT, bool LN, int CPT, int PF, bool HAS_DR>
+__device__ __forceinline__ void bwd_load_step(const BwdArgs& a, int64_t row0, int64_t row_end,
+                                              const int (&col)[CPT],
+                                              BwdRow<CPT, Act<DT>::E> (&rows)[PF]) {
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+        const int64_t r = row0 + p;
+        bwd_load<DT, LN, CPT, HAS_DR>(a, r < row_end ? r : a.R - 1, col, rows[p]);
+    }
+}
+
+// A workgroup holds RG row groups of TPR lanes and walks a tile of
+// rows_per_block rows.  In each step every row group takes PF rows whose loads
+// are all in flight together, reduces the PF rows' two sums in one pass, then
+// writes their gradients.  With PIPE the next step's loads are issued before
+// this step is computed.  dgamma (and dbeta) accumulate in registers.
+template <int DT, int NORM, int TPR, int CPT, int RG, int PF, bool PIPE, bool HAS_DR>
+__global__ __launch_bounds__(RG* TPR) void sp_bwd_kernel(const BwdArgs a) {
     using A = Act<DT>;
+    constexpr bool LN = NORM == SP_LAYERNORM;
     constexpr int E = A::E;
     constexpr int EB = A::kBytes;
-    constexpr int RPW = BLOCK / TPR;
+    constexpr int BLOCK = RG * TPR;
+    constexpr int STEP = RG * PF;  // rows per step of the workgroup
+    constexpr int NACC = LN ? 2 : 1;
     using MW = MaskWord<E>;
-    extern __shared__ float comb[];  // [RPW][nacc][H] when RPW > 1
+    extern __shared__ float comb[];  // [RG][NACC][H] when RG > 1
 
     const int tid = threadIdx.x;
     const int rg = tid / TPR;
     const int l = tid % TPR;
-    const bool ln = a.norm == SP_LAYERNORM;
     const int64_t row_begin = (int64_t)blockIdx.x * a.rows_per_block;
     const int64_t row_end = min(row_begin + a.rows_per_block, a.R);
-    const int iters = (int)((a.rows_per_block + RPW - 1) / RPW);  // uniform over the grid
+    const int iters = (int)((a.rows_per_block + STEP - 1) / STEP);  // uniform over the grid
 
     int col[CPT];
     bool ok[CPT];
@@ -527,85 +548,97 @@ __global__ __launch_bounds__(BLOCK) void sp_bwd_kernel(const BwdArgs a) {
 #pragma unroll
     for (int k = 0; k < CPT; ++k) load_vec_f32<E>(a.gamma, col[k], gam[k]);
 
-    float dg[CPT][E], db[CPT][E];
+    float dg[CPT][E], db[CPT][LN ? E : 1];
 #pragma unroll
-    for (int k = 0; k < CPT; ++k)
+    for (int k = 0; k < CPT; ++k) {
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            dg[k][e] = 0.0f;
-            db[k][e] = 0.0f;
-        }
-
-    BwdRow<DT, CPT, E> cur, nxt;
-    {
-        const int64_t r = row_begin + rg;
-        bwd_load<DT, TPR, CPT, BLOCK, HAS_DR>(a, r < row_end ? r : a.R - 1, col, cur);
+        for (int e = 0; e < E; ++e) dg[k][e] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < (LN ? E : 1); ++e) db[k][e] = 0.0f;
     }
+
+    BwdRow<CPT, E> rows[PF];
+    bwd_load_step<DT, LN, CPT, PF, HAS_DR>(a, row_begin + (int64_t)rg * PF, row_end, col, rows);
     for (int it = 0; it < iters; ++it) {
-        const int64_t row = row_begin + (int64_t)it * RPW + rg;
-        const bool row_ok = row < row_end;
-        // prefetch the next row of this row group while this one is computed
-        if (it + 1 < iters) {
-            const int64_t rn = row + RPW;
-            bwd_load<DT, TPR, CPT, BLOCK, HAS_DR>(a, rn < row_end ? rn : a.R - 1, col, nxt);
+        const int64_t row0 = row_begin + (int64_t)it * STEP + (int64_t)rg * PF;
+        BwdRow<CPT, E> nxt[PIPE ? PF : 1];
+        if constexpr (PIPE) {
+            if (it + 1 < iters)
+                bwd_load_step<DT, LN, CPT, PF, HAS_DR>(a, row0 + STEP, row_end, col, nxt);
         }
-        float xh[CPT][E], g[CPT][E], dyv[CPT][E];
-        float s[2] = {0.0f, 0.0f};
+        // pass 1: the two row sums of every row, and the dgamma / dbeta terms
+        float s[2 * PF];
 #pragma unroll
-        for (int k = 0; k < CPT; ++k) {
-            float hv[E];
-            A::unpack(cur.dy[k], dyv[k]);
-            A::unpack(cur.hh[k], hv);
+        for (int p = 0; p < PF; ++p) {
+            const bool row_ok = row0 + p < row_end;
+            s[2 * p] = 0.0f;
+            s[2 * p + 1] = 0.0f;
 #pragma unroll
-            for (int e = 0; e < E; ++e) {
-                xh[k][e] = (hv[e] - cur.mu) * cur.rs;
-                g[k][e] = dyv[k][e] * gam[k][e];
-            }
-            if (ok[k]) {
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    s[0] += g[k][e];
-                    s[1] += g[k][e] * xh[k][e];
-                }
-                if (row_ok) {
+            for (int k = 0; k < CPT; ++k) {
+                float dyv[E], hv[E];
+                A::unpack(rows[p].dy[k], dyv);
+                A::unpack(rows[p].hh[k], hv);
+                if (ok[k]) {
 #pragma unroll
                     for (int e = 0; e < E; ++e) {
-                        dg[k][e] += dyv[k][e] * xh[k][e];
-                        db[k][e] += dyv[k][e];
+                        const float x = (hv[e] - rows[p].mu) * rows[p].rs;
+                        const float g = dyv[e] * gam[k][e];
+                        if constexpr (LN) s[2 * p] += g;
+                        s[2 * p + 1] += g * x;
+                        if (row_ok) {
+                            dg[k][e] += dyv[e] * x;
+                            if constexpr (LN) db[k][e] += dyv[e];
+                        }
                     }
                 }
             }
         }
-        group_sum<TPR, BLOCK, 2>(s);
-        const float c1 = ln ? s[0] * a.inv_h : 0.0f;
-        const float c2 = s[1] * a.inv_h;
-        const int64_t row_elem = (row_ok ? row : 0) * (int64_t)a.H;
+        group_sum<TPR, BLOCK, 2 * PF>(s);
+        // pass 2: dh, d_residual, dP
 #pragma unroll
-        for (int k = 0; k < CPT; ++k) {
-            float dh[E], dp[E];
-            bool keep[E];
-            MW::unmake(cur.m[k], keep);
-            float drv[E];
-            if constexpr (HAS_DR) A::unpack(cur.dr[k], drv);
+        for (int p = 0; p < PF; ++p) {
+            const int64_t row = row0 + p;
+            const bool row_ok = row < row_end;
+            const float c1 = LN ? s[2 * p] * a.inv_h : 0.0f;
+            const float c2 = s[2 * p + 1] * a.inv_h;
+            const int64_t row_elem = (row_ok ? row : 0) * (int64_t)a.H;
 #pragma unroll
-            for (int e = 0; e < E; ++e) {
-                float v = cur.rs * (g[k][e] - c1 - xh[k][e] * c2);
-                if constexpr (HAS_DR) v += drv[e];
-                dh[e] = v;
-                dp[e] = keep[e] ? v * a.scale : 0.0f;
-            }
-            if (row_ok && ok[k]) {
-                const int64_t off = (row_elem + col[k]) * EB;
-                st16(a.dres, off, A::pack(dh));
-                st16(a.dP, off, A::pack(dp));
+            for (int k = 0; k < CPT; ++k) {
+                float dyv[E], hv[E], drv[E], dh[E], dp[E];
+                bool keep[E];
+                A::unpack(rows[p].dy[k], dyv);
+                A::unpack(rows[p].hh[k], hv);
+                if constexpr (HAS_DR) A::unpack(rows[p].dr[k], drv);
+                MW::unmake(rows[p].m[k], keep);
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float x = (hv[e] - rows[p].mu) * rows[p].rs;
+                    const float g = dyv[e] * gam[k][e];
+                    float v = rows[p].rs * (g - c1 - x * c2);
+                    if constexpr (HAS_DR) v += drv[e];
+                    dh[e] = v;
+                    dp[e] = keep[e] ? v * a.scale : 0.0f;
+                }
+                if (row_ok && ok[k]) {
+                    const int64_t off = (row_elem + col[k]) * EB;
+                    st16(a.dres, off, A::pack(dh));
+                    st16(a.dP, off, A::pack(dp));
+                }
             }
         }
-        if (it + 1 < iters) cur = nxt;
+        if (it + 1 < iters) {
+            if constexpr (PIPE) {
+#pragma unroll
+                for (int p = 0; p < PF; ++p) rows[p] = nxt[p];
+            } else {
+                bwd_load_step<DT, LN, CPT, PF, HAS_DR>(a, row0 + STEP, row_end, col, rows);
+            }
+        }
     }
 
     // ---- this workgroup's partial dgamma / dbeta row ----
-    float* out = a.ws + (int64_t)blockIdx.x * a.nacc * a.H;
-    if constexpr (RPW == 1) {
+    float* out = a.ws + (int64_t)blockIdx.x * NACC * a.H;
+    if constexpr (RG == 1) {
 #pragma unroll
         for (int k = 0; k < CPT; ++k) {
             if (!ok[k]) continue;
@@ -613,7 +646,7 @@ __global__ __launch_bounds__(BLOCK) void sp_bwd_kernel(const BwdArgs a) {
             for (int q = 0; q < E / 4; ++q) {
                 f32x4 v = {dg[k][4 * q], dg[k][4 * q + 1], dg[k][4 * q + 2], dg[k][4 * q + 3]};
                 *reinterpret_cast<f32x4*>(out + col[k] + 4 * q) = v;
-                if (ln) {
+                if constexpr (LN) {
                     f32x4 w = {db[k][4 * q], db[k][4 * q + 1], db[k][4 * q + 2], db[k][4 * q + 3]};
                     *reinterpret_cast<f32x4*>(out + a.H + col[k] + 4 * q) = w;
                 }
@@ -621,22 +654,22 @@ __global__ __launch_bounds__(BLOCK) void sp_bwd_kernel(const BwdArgs a) {
         }
     } else {
         const int H = a.H;
-        float* mine = comb + (int64_t)rg * a.nacc * H;
+        float* mine = comb + (int64_t)rg * NACC * H;
 #pragma unroll
         for (int k = 0; k < CPT; ++k) {
             if (!ok[k]) continue;
 #pragma unroll
             for (int e = 0; e < E; ++e) {
                 mine[col[k] + e] = dg[k][e];
-                if (ln) mine[H + col[k] + e] = db[k][e];
+                if constexpr (LN) mine[H + col[k] + e] = db[k][e];
             }
         }
         __syncthreads();
-        const int n = a.nacc * H;
+        const int n = NACC * H;
         for (int c = tid; c < n; c += BLOCK) {
             float v = comb[c];
 #pragma unroll
-            for (int q = 1; q < RPW; ++q) v += comb[(int64_t)q * n + c];
+            for (int q = 1; q < RG; ++q) v += comb[(int64_t)q * n + c];
             out[c] = v;
         }
     }
@@ -703,7 +736,10 @@ constexpr Layout kLayouts[] = {
 };
 constexpr int kNumLayouts = sizeof(kLayouts) / sizeof(kLayouts[0]);
 constexpr int kNumDefault = 12;
-constexpr int kSubWaveBlock = 256;  // block size of the layouts whose rows fit in one wavefront
+#ifndef SP_SUBWAVE_BLOCK
+#define SP_SUBWAVE_BLOCK 256
+#endif
+constexpr int kSubWaveBlock = SP_SUBWAVE_BLOCK;  // block size of the layouts whose rows fit in one wavefront
 
 constexpr int block_of(int tpr) { return tpr <= kWave ? kSubWaveBlock : tpr; }
 
@@ -711,9 +747,25 @@ constexpr int block_of(int tpr) { return tpr <= kWave ? kSubWaveBlock : tpr; }
 #ifndef SP_FWD_LAYOUT
 #define SP_FWD_LAYOUT -1
 #endif
-#ifndef SP_BWD_LAYOUT
-#define SP_BWD_LAYOUT -1
+#ifndef SP_BWD_VARIANT
+#define SP_BWD_VARIANT -1
 #endif
+
+// Backward launch variants: (lanes per row, chunks per lane, row groups per
+// workgroup, rows in flight per row group).  Entries 0..kNumBwdDefault-1 are
+// the default choices in increasing capacity; the rest are tuning alternatives.
+struct BwdVariant {
+    int tpr, cpt, rg, pf, pipe;
+};
+constexpr BwdVariant kBwdVariants[] = {
+    {16, 1, 16, 1, 0},  {32, 1, 8, 1, 0},   {64, 1, 4, 1, 0},   {32, 3, 8, 1, 0},
+    {64, 2, 4, 1, 0},   {64, 3, 4, 1, 0},   {64, 4, 4, 1, 0},   {512, 1, 1, 2, 0},
+    {512, 2, 1, 2, 0},  {512, 4, 1, 1, 0},  {1024, 4, 1, 1, 0}, {1024, 8, 1, 1, 0},
+    {512, 1, 2, 1, 0},  {512, 1, 1, 4, 0},  {512, 1, 1, 1, 1},  {512, 1, 1, 2, 1},
+    {512, 2, 1, 1, 1},  {512, 2, 1, 1, 0},  {512, 2, 2, 1, 0},  {32, 3, 8, 1, 1},
+};
+constexpr int kNumBwdVariants = sizeof(kBwdVariants) / sizeof(kBwdVariants[0]);
+constexpr int kNumBwdDefault = 12;
 
 typedef void (*FwdKernel)(FwdArgs);
 typedef void (*BwdKernel)(BwdArgs);
@@ -726,7 +778,18 @@ typedef void (*BwdKernel)(BwdArgs);
         X(256, 2, __VA_ARGS__), X(256, 4, __VA_ARGS__), X(1024, 1, __VA_ARGS__), X(128, 8, __VA_ARGS__)
 
 #define SP_FWD_ENTRY(TPR, CPT, DT, TT) &sp_fwd_kernel<DT, TT, TPR, CPT, block_of(TPR)>
-#define SP_BWD_ENTRY(TPR, CPT, DT, HDR) &sp_bwd_kernel<DT, TPR, CPT, block_of(TPR), HDR>
+#define SP_BWD_LIST(X, ...)                                                                      \
+    X(16, 1, 16, 1, 0, __VA_ARGS__), X(32, 1, 8, 1, 0, __VA_ARGS__), X(64, 1, 4, 1, 0, __VA_ARGS__), \
+        X(32, 3, 8, 1, 0, __VA_ARGS__), X(64, 2, 4, 1, 0, __VA_ARGS__),                              \
+        X(64, 3, 4, 1, 0, __VA_ARGS__), X(64, 4, 4, 1, 0, __VA_ARGS__),                              \
+        X(512, 1, 1, 2, 0, __VA_ARGS__), X(512, 2, 1, 2, 0, __VA_ARGS__),                            \
+        X(512, 4, 1, 1, 0, __VA_ARGS__), X(1024, 4, 1, 1, 0, __VA_ARGS__),                           \
+        X(1024, 8, 1, 1, 0, __VA_ARGS__), X(512, 1, 2, 1, 0, __VA_ARGS__),                           \
+        X(512, 1, 1, 4, 0, __VA_ARGS__), X(512, 1, 1, 1, 1, __VA_ARGS__),                            \
+        X(512, 1, 1, 2, 1, __VA_ARGS__), X(512, 2, 1, 1, 1, __VA_ARGS__),                            \
+        X(512, 2, 1, 1, 0, __VA_ARGS__), X(512, 2, 2, 1, 0, __VA_ARGS__), X(32, 3, 8, 1, 1, __VA_ARGS__)
+#define SP_BWD_ENTRY(TPR, CPT, RG, PF, PIPE, DT, NORM, HDR) \
+    &sp_bwd_kernel<DT, NORM, TPR, CPT, RG, PF, PIPE != 0, HDR>
 
 const FwdKernel kFwdBf16[5][kNumLayouts] = {
     {SP_LAYOUT_LIST(SP_FWD_ENTRY, SP_BF16, 0)}, {SP_LAYOUT_LIST(SP_FWD_ENTRY, SP_BF16, 1)},
@@ -734,9 +797,16 @@ const FwdKernel kFwdBf16[5][kNumLayouts] = {
     {SP_LAYOUT_LIST(SP_FWD_ENTRY, SP_BF16, 8)},
 };
 const FwdKernel kFwdF32[kNumLayouts] = {SP_LAYOUT_LIST(SP_FWD_ENTRY, SP_F32, 0)};
-const BwdKernel kBwd[2][2][kNumLayouts] = {
-    {{SP_LAYOUT_LIST(SP_BWD_ENTRY, SP_F32, false)}, {SP_LAYOUT_LIST(SP_BWD_ENTRY, SP_F32, true)}},
-    {{SP_LAYOUT_LIST(SP_BWD_ENTRY, SP_BF16, false)}, {SP_LAYOUT_LIST(SP_BWD_ENTRY, SP_BF16, true)}},
+// [dtype][norm][has dR][variant]
+const BwdKernel kBwd[2][2][2][kNumBwdVariants] = {
+    {{{SP_BWD_LIST(SP_BWD_ENTRY, SP_F32, SP_RMSNORM, false)},
+      {SP_BWD_LIST(SP_BWD_ENTRY, SP_F32, SP_RMSNORM, true)}},
+     {{SP_BWD_LIST(SP_BWD_ENTRY, SP_F32, SP_LAYERNORM, false)},
+      {SP_BWD_LIST(SP_BWD_ENTRY, SP_F32, SP_LAYERNORM, true)}}},
+    {{{SP_BWD_LIST(SP_BWD_ENTRY, SP_BF16, SP_RMSNORM, false)},
+      {SP_BWD_LIST(SP_BWD_ENTRY, SP_BF16, SP_RMSNORM, true)}},
+     {{SP_BWD_LIST(SP_BWD_ENTRY, SP_BF16, SP_LAYERNORM, false)},
+      {SP_BWD_LIST(SP_BWD_ENTRY, SP_BF16, SP_LAYERNORM, true)}}},
 };
 
 // ---------------------------------------------------------------------------
@@ -807,10 +877,19 @@ int fwd_tt_index(int T) {
     }
 }
 
+int pick_bwd_variant(int64_t nchunk, int forced) {
+    auto cap = [](int v) { return kBwdVariants[v].tpr * kBwdVariants[v].cpt; };
+    if (forced >= 0 && forced < kNumBwdVariants && nchunk <= cap(forced)) return forced;
+    for (int i = 0; i < kNumBwdDefault; ++i)
+        if (nchunk <= cap(i)) return i;
+    return -1;
+}
+
 struct BwdPlan {
-    int layout;
+    int variant;
     int64_t rows_per_block;
     int64_t blocks;
+    int block;
     int nacc;
     size_t ws_bytes;
     size_t lds_bytes;
@@ -820,18 +899,19 @@ BwdPlan plan_bwd(const sp_desc_t* d) {
     BwdPlan p{};
     const int64_t R = shard_rows(d);
     const int64_t nchunk = d->H / elems_per_chunk(d->dtype);
-    p.layout = pick_layout(nchunk, SP_BWD_LAYOUT);
-    if (p.layout < 0) return p;  // unreachable for a validated descriptor
-    const int tpr = kLayouts[p.layout].tpr;
-    const int rpw = block_of(tpr) / tpr;
+    p.variant = pick_bwd_variant(nchunk, SP_BWD_VARIANT);
+    if (p.variant < 0) return p;  // unreachable for a validated descriptor
+    const BwdVariant v = kBwdVariants[p.variant];
+    const int step = v.rg * v.pf;  // rows a workgroup takes per step
+    p.block = v.rg * v.tpr;
     p.nacc = d->norm == SP_LAYERNORM ? 2 : 1;
     int64_t rpb = (R + SP_BWD_TARGET_BLOCKS - 1) / SP_BWD_TARGET_BLOCKS;
-    rpb = ((rpb + rpw - 1) / rpw) * rpw;
-    if (rpb < rpw) rpb = rpw;
+    rpb = ((rpb + step - 1) / step) * step;
+    if (rpb < step) rpb = step;
     p.rows_per_block = rpb;
     p.blocks = R > 0 ? (R + rpb - 1) / rpb : 0;
     p.ws_bytes = (size_t)p.blocks * (size_t)p.nacc * (size_t)d->H * sizeof(float);
-    p.lds_bytes = rpw > 1 ? (size_t)rpw * (size_t)p.nacc * (size_t)d->H * sizeof(float) : 0;
+    p.lds_bytes = v.rg > 1 ? (size_t)v.rg * (size_t)p.nacc * (size_t)d->H * sizeof(float) : 0;
     return p;
 }
 
@@ -1026,13 +1106,13 @@ extern "C" int sp_region_bwd(const sp_desc_t* d, const void* dY, const void* h, 
     a.scale = (float)(1.0 / (1.0 - (double)d->p));
     a.inv_h = (float)(1.0 / (double)H);
 
-    if (plan.layout < 0) return SP_ESHAPE;
+    if (plan.variant < 0) return SP_ESHAPE;
     if (plan.blocks > INT32_MAX) return SP_ESHAPE;
     (void)hipGetLastError();
     if (plan.blocks > 0) {
-        const Layout L = kLayouts[plan.layout];
-        const BwdKernel k = kBwd[d->dtype == SP_BF16 ? 1 : 0][dR ? 1 : 0][plan.layout];
-        hipLaunchKernelGGL(k, dim3((unsigned)plan.blocks), dim3(block_of(L.tpr)),
+        const BwdKernel k =
+            kBwd[d->dtype == SP_BF16 ? 1 : 0][d->norm == SP_LAYERNORM ? 1 : 0][dR ? 1 : 0][plan.variant];
+        hipLaunchKernelGGL(k, dim3((unsigned)plan.blocks), dim3(plan.block),
                            (unsigned)plan.lds_bytes, (hipStream_t)stream, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return record_hip(e);
