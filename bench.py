@@ -35,8 +35,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 DEFAULT_WORKLOAD = "layernorm_T8_S4096_B1_H4096"
-SECONDARY = ["minimind_T2_S2048_B2_H768", "large_hidden_T8_S8192_B2_H8192",
-             "long_seq_T8_S32768_B1_H8192"]
+# (workload, descriptor flags): the other workloads, and the headline and large-hidden shards
+# with the mask regenerated in the backward instead of stored (SP_FLAG_RECOMPUTE_MASK)
+SECONDARY = [("minimind_T2_S2048_B2_H768", 0), ("large_hidden_T8_S8192_B2_H8192", 0),
+             ("long_seq_T8_S32768_B1_H8192", 0), (DEFAULT_WORKLOAD, 1),
+             ("large_hidden_T8_S8192_B2_H8192", 1)]
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
 ROTATE_BYTES = 1.5e9
 PROFILES = os.path.join(ROOT, "profiles")
@@ -81,7 +84,7 @@ def load_traffic(workload):
 class ShardBuffers:
     """Per-shard inputs and outputs of one buffer set."""
 
-    def __init__(self, sp, w, j, src, P):
+    def __init__(self, sp, w, j, src, P, flags=0):
         import torch
         dev, act, R, H = "cuda", w.torch_dtype, w.R, w.H
         ln = w.norm == "ln"
@@ -93,14 +96,15 @@ class ShardBuffers:
         self.beta = src["beta"]
         self.h = torch.empty((R, H), dtype=act, device=dev)
         self.y = torch.empty((R, H), dtype=act, device=dev)
-        self.mask = torch.empty((R, H), dtype=torch.uint8, device=dev)
+        regen = flags & sp.SP_FLAG_RECOMPUTE_MASK
+        self.mask = None if regen else torch.empty((R, H), dtype=torch.uint8, device=dev)
         self.mean = torch.empty(R, device=dev) if ln else None
         self.rstd = torch.empty(R, device=dev)
         self.dres = torch.empty((R, H), dtype=act, device=dev)
         self.dP = torch.empty((R, H), dtype=act, device=dev)
         self.dgamma = torch.empty(H, device=dev)
         self.dbeta = torch.empty(H, device=dev) if ln else None
-        self.desc = sp.make_desc(w.S, w.B, w.H, w.T, j, w.dtype, w.norm, w.eps, w.p, w.seed)
+        self.desc = sp.make_desc(w.S, w.B, w.H, w.T, j, w.dtype, w.norm, w.eps, w.p, w.seed, flags)
         self.ws_bytes = max(16, sp.sp_region_bwd_workspace_size(self.desc))
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
 
@@ -115,9 +119,9 @@ class ShardBuffers:
 class BufferSet:
     """One disjoint set: its own copy of the full partial buffers and the shards' tensors."""
 
-    def __init__(self, sp, w, shards, src):
+    def __init__(self, sp, w, shards, src, flags=0):
         self.P = [p.clone() for p in src["P"]]
-        self.shards = [ShardBuffers(sp, w, j, src, self.P) for j in shards]
+        self.shards = [ShardBuffers(sp, w, j, src, self.P, flags) for j in shards]
 
     def prepare(self, sp, stream):
         for s in self.shards:
@@ -145,20 +149,21 @@ def make_source(w, shards):
     return src
 
 
-def measure(sp, w, shards, K, Wm, stream):
+def measure(sp, w, shards, K, Wm, stream, flags=0):
     """Time K steps (graph replay, host clock) and per-launch durations (events)."""
     import torch
 
     src = make_source(w, shards)
     fwd_b = bwd_b = 0
     for j in shards:
-        f, b = sp.sp_region_traffic_bytes(sp.make_desc(w.S, w.B, w.H, w.T, j, w.dtype, w.norm))
+        f, b = sp.sp_region_traffic_bytes(sp.make_desc(w.S, w.B, w.H, w.T, j, w.dtype, w.norm,
+                                                       flags=flags))
         fwd_b += f
         bwd_b += b
     step_bytes = fwd_b + bwd_b
     n_sets = max(2, math.ceil(ROTATE_BYTES / step_bytes))
     n_sets = min(n_sets, max(2, K))
-    sets = [BufferSet(sp, w, shards, src) for _ in range(n_sets)]
+    sets = [BufferSet(sp, w, shards, src, flags) for _ in range(n_sets)]
     for s in sets:
         s.prepare(sp, stream.cuda_stream)
     torch.cuda.synchronize()  # the copies above ran on torch's current stream, not on `stream`
@@ -182,8 +187,9 @@ def measure(sp, w, shards, K, Wm, stream):
     torch.cuda.synchronize()
 
     # graph replays must reproduce the eager results bit for bit
-    keys = ("h", "y", "mask", "rstd", "dres", "dP", "dgamma")
     first = sets[0].shards[0]
+    keys = tuple(k for k in ("h", "y", "mask", "rstd", "dres", "dP", "dgamma")
+                 if getattr(first, k) is not None)
     ref = {k: getattr(first, k).clone() for k in keys}
     graph_bad = set()
     for _ in range(2):
@@ -444,12 +450,13 @@ def main():
     del src, sets
     torch.cuda.empty_cache()
     if not args.no_secondary:
-        for name in SECONDARY:
+        for name, flags in SECONDARY:
             ws = W.WORKLOADS[name]
             shards = ws.shards if len(ws.shards) > 2 else (ws.shards[0],)
             K2 = 40 if len(shards) > 2 else 400
-            r, s2, st2 = measure(sp, ws, tuple(shards), K2, max(10, K2 // 10), stream)
-            line["workloads"][name] = {
+            r, s2, st2 = measure(sp, ws, tuple(shards), K2, max(10, K2 // 10), stream, flags)
+            label = name + ("+recompute_mask" if flags & sp.SP_FLAG_RECOMPUTE_MASK else "")
+            line["workloads"][label] = {
                 "shards_per_step": len(shards), "steps": K2,
                 "GBs": round(r["value_GBs"], 1), "pct_of_peak": round(100 * r["value_GBs"] / PEAK_HBM_GBS, 2),
                 "ms_per_step": round(r["ms_per_step"], 5), "tokens_per_s": round(r["tokens_per_s"], 1),

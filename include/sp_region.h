@@ -58,6 +58,14 @@ extern "C" {
 enum { SP_F32 = 0, SP_BF16 = 1 };
 /* normalisation */
 enum { SP_RMSNORM = 0, SP_LAYERNORM = 1 };
+/* descriptor flags */
+enum {
+    /* Keep no mask tensor: the forward stores none (mask_out must be NULL) and the
+     * backward regenerates the keep flags from (seed, global index) (mask must be
+     * NULL).  Saves one byte per element in each direction; the flags are the same
+     * bits either way. */
+    SP_FLAG_RECOMPUTE_MASK = 1
+};
 /* status codes */
 enum {
     SP_OK = 0,
@@ -79,6 +87,8 @@ typedef struct sp_desc {
     float eps;         /* added to the mean square / variance; finite, >= 0 */
     float p;           /* dropout probability, 0 <= p < 1 */
     uint64_t seed;     /* dropout generator key */
+    uint32_t flags;    /* SP_FLAG_* bits; unknown bits are rejected (SP_EPARAM) */
+    uint32_t reserved; /* must be 0 */
 } sp_desc_t;
 
 /*
@@ -102,7 +112,7 @@ typedef struct sp_desc {
  * gamma     [H] fp32.  beta: [H] fp32 for LayerNorm, NULL for RMSNorm.
  * h_out     shard: the residual stream after the add (saved for the backward).
  * y_out     shard: the normalised output (what the next all-gather consumes).
- * mask_out  shard of bytes, 1 = kept, 0 = dropped.
+ * mask_out  shard of bytes, 1 = kept, 0 = dropped (NULL with SP_FLAG_RECOMPUTE_MASK).
  * mean_out  [R] fp32 for LayerNorm, NULL for RMSNorm.
  * rstd_out  [R] fp32.
  */
@@ -125,8 +135,9 @@ int sp_region_fwd(const sp_desc_t* d, const void* const* P, const void* residual
  *   the norm weights are replicated, so the partials of all shards still have to
  *   be summed across ranks)
  *
- * dY        shard gradient of y.  h, mask, mean (LayerNorm; NULL for RMSNorm),
- *           rstd: as saved by sp_region_fwd.  gamma: [H] fp32.
+ * dY        shard gradient of y.  h, mask (NULL with SP_FLAG_RECOMPUTE_MASK), mean
+ *           (LayerNorm; NULL for RMSNorm), rstd: as saved by sp_region_fwd.
+ *           gamma: [H] fp32.
  * dR        optional shard: an extra gradient of the residual stream h from its
  *           other consumer (the next residual add); NULL = none.
  * d_residual, dP   shard outputs, activation type.
@@ -147,7 +158,8 @@ size_t sp_region_bwd_workspace_size(const sp_desc_t* d);
 /*
  * Algorithmic HBM bytes of one call: every input read once and every output
  * written once (fwd: T partial slabs, residual, h, y, mask, stats, gamma/beta;
- * bwd: dY, h, mask, stats, gamma, d_residual, dP, dgamma/dbeta; dR not counted).
+ * bwd: dY, h, mask, stats, gamma, d_residual, dP, dgamma/dbeta; dR not counted;
+ * no mask bytes with SP_FLAG_RECOMPUTE_MASK).
  * Returns SP_OK or the validation error of the descriptor.
  */
 int sp_region_traffic_bytes(const sp_desc_t* d, uint64_t* fwd_bytes, uint64_t* bwd_bytes);

@@ -97,6 +97,7 @@ def bwd_call(desc, ws_bytes=None, **over):
     (dict(H=100), -2),                      # bf16 row not a multiple of 16 bytes
     (dict(H=6, dtype="f32"), -2),           # fp32 row not a multiple of 16 bytes
     (dict(H=65536 + 8), -2),                # row above SP_MAX_H_BYTES
+    (dict(flags=2), -4), (dict(flags=0x80000000), -4),  # unknown flag bits
 ])
 def test_descriptor_errors(lib, kw, code):
     d = good_desc(**kw)
@@ -105,6 +106,29 @@ def test_descriptor_errors(lib, kw, code):
     f, b = ctypes.c_uint64(), ctypes.c_uint64()
     assert lib.sp_region_traffic_bytes(ctypes.byref(d), ctypes.byref(f), ctypes.byref(b)) == code
     assert sp.sp_region_bwd_workspace_size(d) == 0
+
+
+def test_reserved_field_must_be_zero(lib):
+    d = good_desc()
+    d.reserved = 1
+    assert fwd_call(d) == -4
+    assert bwd_call(d) == -4
+
+
+def test_recompute_mask_flag_pointer_rules(lib):
+    d = good_desc(flags=sp.SP_FLAG_RECOMPUTE_MASK)
+    assert fwd_call(d) == -1                                   # a mask tensor given anyway
+    assert bwd_call(d) == -1
+    plain = good_desc()
+    assert sp.sp_region_fwd(plain, [fake(10 + t) for t in range(4)], fake(1), fake(2), None,
+                            fake(4), fake(5), None, None, fake(8), stream=0) == -1  # mask missing
+    # without a mask tensor the empty shard is still a no-op
+    assert sp.sp_region_fwd(good_desc(S=0, flags=1), [fake(10 + t) for t in range(4)], fake(1),
+                            fake(2), None, fake(4), fake(5), None, None, fake(8), stream=0) == 0
+    f0, b0 = sp.sp_region_traffic_bytes(plain)
+    f1, b1 = sp.sp_region_traffic_bytes(d)
+    N = plain.R * plain.H
+    assert (f0 - f1, b0 - b1) == (N, N)                        # one byte per element each way
 
 
 def test_null_descriptor(lib):

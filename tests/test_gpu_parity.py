@@ -294,6 +294,9 @@ EDGE = [
     (2, 6, 1, 65536, "bf16", "rms", 0.1, 1),    # the longest bf16 row
     (2, 4, 1, 32768, "f32", "ln", 0.1, 0),      # the longest fp32 row
     (4, 4096, 4, 128, "bf16", "ln", 0.1, 2),    # many short rows
+    (4, 400, 3, 2056, "bf16", "ln", 0.1, 1),    # 257 chunks: one ragged chunk past 256
+    (2, 200, 1, 8192, "bf16", "ln", 0.2, 1),    # 1024-chunk rows, 100 rows
+    (8, 64, 1, 4096, "bf16", "ln", 0.1, 5),     # 8 rows
 ]
 
 
@@ -317,10 +320,10 @@ def test_edge_shapes_match_oracle(T, S, B, H, dtype, norm, p, j):
         assert bool(g["mask"].all())
 
 
-@pytest.mark.parametrize("norm", ["rms", "ln"])
-def test_residual_gradient_input(norm):
-    print(f"\n[case] dR input, {norm}", flush=True)
-    c = _edge_case(4, 64, 2, 1024, "bf16", norm, 0.2, 1)
+@pytest.mark.parametrize("norm,H", [("rms", 1024), ("ln", 1024), ("ln", 4096)])
+def test_residual_gradient_input(norm, H):
+    print(f"\n[case] dR input, {norm}, H={H}", flush=True)
+    c = _edge_case(4, 64, 2, H, "bf16", norm, 0.2, 1)
     j = 1
     dR_full = W._randn((c.w.S, c.w.B, c.w.H), 1.0, "cpu", 4242).to(torch.bfloat16)
     dR = c.shard(dR_full, j).cuda()
@@ -428,3 +431,27 @@ def test_graph_replays_match_eager():
         for k in ref:
             assert torch.equal(ref[k], got[k]), (rep, k)
         del other
+
+
+@pytest.mark.parametrize("name,j", [("layernorm_T8_S4096_B1_H4096", 3), ("minimind_T2_S2048_B2_H768", 1)])
+def test_recomputed_mask_matches_stored_mask(name, j):
+    """With SP_FLAG_RECOMPUTE_MASK the forward keeps no mask and the backward
+    regenerates the flags: every output is bit-identical to the stored-mask run,
+    and the backward matches the oracle (which uses its own stored mask)."""
+    print(f"\n[case] {name} shard {j}: recomputed mask", flush=True)
+    w = W.WORKLOADS[name]
+    c = Case(w, "cpu")
+    f = gpu_fwd(c, j)
+    b = gpu_bwd(c, j, f)
+    d = sp.make_desc(w.S, w.B, w.H, w.T, j, w.dtype, w.norm, w.eps, w.p, w.seed,
+                     flags=sp.SP_FLAG_RECOMPUTE_MASK)
+    f2 = sp.forward(d, c.P, c.shard(c.res, j), c.gamma, c.beta)
+    assert f2["mask"] is None
+    b2 = sp.backward(d, c.shard(c.dY, j), f2["h"], None, f2["mean"], f2["rstd"], c.gamma)
+    torch.cuda.synchronize()
+    for k in ("h", "y", "rstd") + (("mean",) if w.norm == "ln" else ()):
+        assert torch.equal(f[k], f2[k]), k
+    for k in ("d_res", "dP", "dgamma") + (("dbeta",) if w.norm == "ln" else ()):
+        assert torch.equal(b[k], b2[k]), k
+    o = oracle_fwd(c, j)
+    compare_bwd(w, b2, oracle_bwd(c, j, o))

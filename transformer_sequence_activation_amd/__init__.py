@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(PKG, "libsp_region.so")
 SP_MAX_T = 64
 SP_F32, SP_BF16 = 0, 1
 SP_RMSNORM, SP_LAYERNORM = 0, 1
+SP_FLAG_RECOMPUTE_MASK = 1
 SP_OK = 0
 STATUS = {0: "SP_OK", -1: "SP_EINVAL", -2: "SP_ESHAPE", -3: "SP_EDTYPE", -4: "SP_EPARAM",
           -5: "SP_EALIGN", -6: "SP_EWORKSPACE", -7: "SP_EHIP"}
@@ -33,6 +34,7 @@ class SpDesc(ctypes.Structure):
         ("dtype", ctypes.c_int32), ("norm", ctypes.c_int32),
         ("eps", ctypes.c_float), ("p", ctypes.c_float),
         ("seed", ctypes.c_uint64),
+        ("flags", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
     ]
 
     @property
@@ -77,10 +79,10 @@ def load(path=LIB_PATH):
     return L
 
 
-def make_desc(S, B, H, T, j, dtype="bf16", norm="rms", eps=1e-6, p=0.1, seed=1234):
+def make_desc(S, B, H, T, j, dtype="bf16", norm="rms", eps=1e-6, p=0.1, seed=1234, flags=0):
     dt = {"bf16": SP_BF16, "f32": SP_F32}.get(dtype, dtype)
     nm = {"rms": SP_RMSNORM, "ln": SP_LAYERNORM}.get(norm, norm)
-    return SpDesc(S, B, H, T, j, dt, nm, eps, p, seed)
+    return SpDesc(S, B, H, T, j, dt, nm, eps, p, seed, flags, 0)
 
 
 def _ptr(x):
@@ -153,15 +155,17 @@ def _act_dtype(desc):
 
 def forward(desc, P, residual, gamma, beta=None, stream=None):
     """P: T full [S,B,H] device tensors; residual: the shard (R*H elements).
-    Returns dict h, y, mask, mean (None for RMSNorm), rstd."""
+    Returns dict h, y, mask (None with SP_FLAG_RECOMPUTE_MASK), mean (None for
+    RMSNorm), rstd."""
     import torch
     dev = residual.device
     R, H = desc.R, desc.H
     act = _act_dtype(desc)
+    keep_mask = not (desc.flags & SP_FLAG_RECOMPUTE_MASK)
     out = {
         "h": torch.empty((R, H), dtype=act, device=dev),
         "y": torch.empty((R, H), dtype=act, device=dev),
-        "mask": torch.empty((R, H), dtype=torch.uint8, device=dev),
+        "mask": torch.empty((R, H), dtype=torch.uint8, device=dev) if keep_mask else None,
         "mean": torch.empty(R, dtype=torch.float32, device=dev) if desc.norm == SP_LAYERNORM else None,
         "rstd": torch.empty(R, dtype=torch.float32, device=dev),
     }

@@ -227,7 +227,7 @@ struct FwdArgs {
     const float* beta;
     void* h;
     void* y;
-    uint8_t* mask;
+    uint8_t* mask;   // NULL: keep no mask
     float* mean;
     float* rstd;
     int64_t R;       // token rows in the shard
@@ -390,7 +390,7 @@ __global__ __launch_bounds__(BLOCK) void sp_fwd_kernel(const FwdArgs a) {
         A::unpack(hp, hv[k]);  // the rounded h the norm sees
         if (row_ok && ok[k]) {
             st16(a.h, idx * EB, hp);
-            *reinterpret_cast<typename MW::type*>(a.mask + idx) = MW::make(keep);
+            if (a.mask) *reinterpret_cast<typename MW::type*>(a.mask + idx) = MW::make(keep);
         }
     }
 
@@ -460,6 +460,8 @@ struct BwdArgs {
     void* dres;
     void* dP;
     float* ws;            // [G][nacc][H] fp32 partial sums of dgamma (, dbeta)
+    uint64_t base;        // global index of the shard's first element (mask regeneration)
+    uint32_t thr, key0, key1;
     int64_t R;
     int64_t rows_per_block;
     int32_t H;
@@ -480,7 +482,7 @@ struct BwdRow {
     float mu, rs;
 };
 
-template <int DT, bool LN, int CPT, bool HAS_DR>
+template <int DT, bool LN, int CPT, bool HAS_DR, bool REGEN>
 __device__ __forceinline__ void bwd_load(const BwdArgs& a, int64_t rowc, const int (&col)[CPT],
                                          BwdRow<CPT, Act<DT>::E>& b) {
     using A = Act<DT>;
@@ -493,7 +495,7 @@ __device__ __forceinline__ void bwd_load(const BwdArgs& a, int64_t rowc, const i
         b.dy[k] = ld16(a.dY, idx * EB);
         b.hh[k] = ld16(a.h, idx * EB);
         if constexpr (HAS_DR) b.dr[k] = ld16(a.dR, idx * EB);
-        b.m[k] = *reinterpret_cast<const typename MaskWord<E>::type*>(a.mask + idx);
+        if constexpr (!REGEN) b.m[k] = *reinterpret_cast<const typename MaskWord<E>::type*>(a.mask + idx);
     }
     b.rs = a.rstd[rowc];
     b.mu = LN ? a.mean[rowc] : 0.0f;
@@ -501,14 +503,14 @@ __device__ __forceinline__ void bwd_load(const BwdArgs& a, int64_t rowc, const i
 
 // The PF rows one row group takes in step `it` (rows past the tile's end are
 // loaded from a valid row and never stored).
-template <int DT, bool LN, int CPT, int PF, bool HAS_DR>
+template <int DT, bool LN, int CPT, int PF, bool HAS_DR, bool REGEN>
 __device__ __forceinline__ void bwd_load_step(const BwdArgs& a, int64_t row0, int64_t row_end,
                                               const int (&col)[CPT],
                                               BwdRow<CPT, Act<DT>::E> (&rows)[PF]) {
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
         const int64_t r = row0 + p;
-        bwd_load<DT, LN, CPT, HAS_DR>(a, r < row_end ? r : a.R - 1, col, rows[p]);
+        bwd_load<DT, LN, CPT, HAS_DR, REGEN>(a, r < row_end ? r : a.R - 1, col, rows[p]);
     }
 }
 
@@ -516,8 +518,10 @@ __device__ __forceinline__ void bwd_load_step(const BwdArgs& a, int64_t row0, in
 // rows_per_block rows.  In each step every row group takes PF rows whose loads
 // are all in flight together, reduces the PF rows' two sums in one pass, then
 // writes their gradients.  With PIPE the next step's loads are issued before
-// this step is computed.  dgamma (and dbeta) accumulate in registers.
-template <int DT, int NORM, int TPR, int CPT, int RG, int PF, bool PIPE, bool HAS_DR>
+// this step is computed.  dgamma (and dbeta) accumulate in registers and each
+// workgroup writes one partial row.  With REGEN the keep flags are generated
+// again from (seed, global index) instead of read from a mask tensor.
+template <int DT, int NORM, int TPR, int CPT, int RG, int PF, bool PIPE, bool HAS_DR, bool REGEN>
 __global__ __launch_bounds__(RG* TPR) void sp_bwd_kernel(const BwdArgs a) {
     using A = Act<DT>;
     constexpr bool LN = NORM == SP_LAYERNORM;
@@ -558,13 +562,13 @@ __global__ __launch_bounds__(RG* TPR) void sp_bwd_kernel(const BwdArgs a) {
     }
 
     BwdRow<CPT, E> rows[PF];
-    bwd_load_step<DT, LN, CPT, PF, HAS_DR>(a, row_begin + (int64_t)rg * PF, row_end, col, rows);
+    bwd_load_step<DT, LN, CPT, PF, HAS_DR, REGEN>(a, row_begin + (int64_t)rg * PF, row_end, col, rows);
     for (int it = 0; it < iters; ++it) {
         const int64_t row0 = row_begin + (int64_t)it * STEP + (int64_t)rg * PF;
         BwdRow<CPT, E> nxt[PIPE ? PF : 1];
         if constexpr (PIPE) {
             if (it + 1 < iters)
-                bwd_load_step<DT, LN, CPT, PF, HAS_DR>(a, row0 + STEP, row_end, col, nxt);
+                bwd_load_step<DT, LN, CPT, PF, HAS_DR, REGEN>(a, row0 + STEP, row_end, col, nxt);
         }
         // pass 1: the two row sums of every row, and the dgamma / dbeta terms
         float s[2 * PF];
@@ -609,7 +613,10 @@ __global__ __launch_bounds__(RG* TPR) void sp_bwd_kernel(const BwdArgs a) {
                 A::unpack(rows[p].dy[k], dyv);
                 A::unpack(rows[p].hh[k], hv);
                 if constexpr (HAS_DR) A::unpack(rows[p].dr[k], drv);
-                MW::unmake(rows[p].m[k], keep);
+                if constexpr (REGEN)
+                    keep_flags<E>(a.base + (uint64_t)(row_elem + col[k]), a.thr, a.key0, a.key1, keep);
+                else
+                    MW::unmake(rows[p].m[k], keep);
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
                     const float x = (hv[e] - rows[p].mu) * rows[p].rs;
@@ -631,7 +638,7 @@ __global__ __launch_bounds__(RG* TPR) void sp_bwd_kernel(const BwdArgs a) {
 #pragma unroll
                 for (int p = 0; p < PF; ++p) rows[p] = nxt[p];
             } else {
-                bwd_load_step<DT, LN, CPT, PF, HAS_DR>(a, row0 + STEP, row_end, col, rows);
+                bwd_load_step<DT, LN, CPT, PF, HAS_DR, REGEN>(a, row0 + STEP, row_end, col, rows);
             }
         }
     }
@@ -752,17 +759,15 @@ constexpr int block_of(int tpr) { return tpr <= kWave ? kSubWaveBlock : tpr; }
 #endif
 
 // Backward launch variants: (lanes per row, chunks per lane, row groups per
-// workgroup, rows in flight per row group).  Entries 0..kNumBwdDefault-1 are
-// the default choices in increasing capacity; the rest are tuning alternatives.
+// workgroup, rows in flight per row group, prefetch of the next step), the
+// default choices in increasing capacity.
 struct BwdVariant {
     int tpr, cpt, rg, pf, pipe;
 };
 constexpr BwdVariant kBwdVariants[] = {
-    {16, 1, 16, 1, 0},  {32, 1, 8, 1, 0},   {64, 1, 4, 1, 0},   {32, 3, 8, 1, 0},
-    {64, 2, 4, 1, 0},   {64, 3, 4, 1, 0},   {64, 4, 4, 1, 0},   {512, 1, 1, 2, 0},
-    {512, 2, 1, 2, 0},  {512, 4, 1, 1, 0},  {1024, 4, 1, 1, 0}, {1024, 8, 1, 1, 0},
-    {512, 1, 2, 1, 0},  {512, 1, 1, 4, 0},  {512, 1, 1, 1, 1},  {512, 1, 1, 2, 1},
-    {512, 2, 1, 1, 1},  {512, 2, 1, 1, 0},  {512, 2, 2, 1, 0},  {32, 3, 8, 1, 1},
+    {16, 1, 16, 1, 0}, {32, 1, 8, 1, 0}, {64, 1, 4, 1, 0},  {32, 3, 8, 1, 0},  {64, 2, 4, 1, 0},
+    {64, 3, 4, 1, 0},  {64, 4, 4, 1, 0}, {512, 1, 1, 2, 0}, {512, 2, 1, 2, 0}, {512, 4, 1, 1, 0},
+    {1024, 4, 1, 1, 0}, {1024, 8, 1, 1, 0},
 };
 constexpr int kNumBwdVariants = sizeof(kBwdVariants) / sizeof(kBwdVariants[0]);
 constexpr int kNumBwdDefault = 12;
@@ -784,12 +789,9 @@ typedef void (*BwdKernel)(BwdArgs);
         X(64, 3, 4, 1, 0, __VA_ARGS__), X(64, 4, 4, 1, 0, __VA_ARGS__),                              \
         X(512, 1, 1, 2, 0, __VA_ARGS__), X(512, 2, 1, 2, 0, __VA_ARGS__),                            \
         X(512, 4, 1, 1, 0, __VA_ARGS__), X(1024, 4, 1, 1, 0, __VA_ARGS__),                           \
-        X(1024, 8, 1, 1, 0, __VA_ARGS__), X(512, 1, 2, 1, 0, __VA_ARGS__),                           \
-        X(512, 1, 1, 4, 0, __VA_ARGS__), X(512, 1, 1, 1, 1, __VA_ARGS__),                            \
-        X(512, 1, 1, 2, 1, __VA_ARGS__), X(512, 2, 1, 1, 1, __VA_ARGS__),                            \
-        X(512, 2, 1, 1, 0, __VA_ARGS__), X(512, 2, 2, 1, 0, __VA_ARGS__), X(32, 3, 8, 1, 1, __VA_ARGS__)
-#define SP_BWD_ENTRY(TPR, CPT, RG, PF, PIPE, DT, NORM, HDR) \
-    &sp_bwd_kernel<DT, NORM, TPR, CPT, RG, PF, PIPE != 0, HDR>
+        X(1024, 8, 1, 1, 0, __VA_ARGS__)
+#define SP_BWD_ENTRY(TPR, CPT, RG, PF, PIPE, DT, NORM, HDR, REGEN) \
+    &sp_bwd_kernel<DT, NORM, TPR, CPT, RG, PF, PIPE != 0, HDR, REGEN>
 
 const FwdKernel kFwdBf16[5][kNumLayouts] = {
     {SP_LAYOUT_LIST(SP_FWD_ENTRY, SP_BF16, 0)}, {SP_LAYOUT_LIST(SP_FWD_ENTRY, SP_BF16, 1)},
@@ -797,17 +799,13 @@ const FwdKernel kFwdBf16[5][kNumLayouts] = {
     {SP_LAYOUT_LIST(SP_FWD_ENTRY, SP_BF16, 8)},
 };
 const FwdKernel kFwdF32[kNumLayouts] = {SP_LAYOUT_LIST(SP_FWD_ENTRY, SP_F32, 0)};
-// [dtype][norm][has dR][variant]
-const BwdKernel kBwd[2][2][2][kNumBwdVariants] = {
-    {{{SP_BWD_LIST(SP_BWD_ENTRY, SP_F32, SP_RMSNORM, false)},
-      {SP_BWD_LIST(SP_BWD_ENTRY, SP_F32, SP_RMSNORM, true)}},
-     {{SP_BWD_LIST(SP_BWD_ENTRY, SP_F32, SP_LAYERNORM, false)},
-      {SP_BWD_LIST(SP_BWD_ENTRY, SP_F32, SP_LAYERNORM, true)}}},
-    {{{SP_BWD_LIST(SP_BWD_ENTRY, SP_BF16, SP_RMSNORM, false)},
-      {SP_BWD_LIST(SP_BWD_ENTRY, SP_BF16, SP_RMSNORM, true)}},
-     {{SP_BWD_LIST(SP_BWD_ENTRY, SP_BF16, SP_LAYERNORM, false)},
-      {SP_BWD_LIST(SP_BWD_ENTRY, SP_BF16, SP_LAYERNORM, true)}}},
-};
+// [dtype][norm][has dR][mask regenerated][variant]
+#define SP_BWD_BY_DR(DT, NORM, HDR) \
+    {{SP_BWD_LIST(SP_BWD_ENTRY, DT, NORM, HDR, false)}, {SP_BWD_LIST(SP_BWD_ENTRY, DT, NORM, HDR, true)}}
+#define SP_BWD_BY_NORM(DT)                                                                       \
+    {{SP_BWD_BY_DR(DT, SP_RMSNORM, false), SP_BWD_BY_DR(DT, SP_RMSNORM, true)},                  \
+     {SP_BWD_BY_DR(DT, SP_LAYERNORM, false), SP_BWD_BY_DR(DT, SP_LAYERNORM, true)}}
+const BwdKernel kBwd[2][2][2][2][kNumBwdVariants] = {SP_BWD_BY_NORM(SP_F32), SP_BWD_BY_NORM(SP_BF16)};
 
 // ---------------------------------------------------------------------------
 // Host-side validation.
@@ -823,6 +821,7 @@ int check_desc(const sp_desc_t* d) {
     if (d->norm != SP_RMSNORM && d->norm != SP_LAYERNORM) return SP_EPARAM;
     if (!(d->p >= 0.0f && d->p < 1.0f)) return SP_EPARAM;
     if (!(d->eps >= 0.0f) || !isfinite(d->eps)) return SP_EPARAM;
+    if ((d->flags & ~(uint32_t)SP_FLAG_RECOMPUTE_MASK) != 0 || d->reserved != 0) return SP_EPARAM;
     if (d->S < 0 || d->B < 0 || d->H <= 0) return SP_ESHAPE;
     if (d->T < 1 || d->T > SP_MAX_T) return SP_ESHAPE;
     if (d->j < 0 || d->j >= d->T) return SP_ESHAPE;
@@ -836,6 +835,9 @@ int check_desc(const sp_desc_t* d) {
 }
 
 inline int64_t shard_rows(const sp_desc_t* d) { return (d->S / d->T) * d->B; }
+
+// keep iff word >= floor(p * 2^32), the product taken in double; p < 1 keeps it below 2^32.
+inline uint32_t keep_threshold(float p) { return (uint32_t)floor((double)p * 4294967296.0); }
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -897,21 +899,21 @@ struct BwdPlan {
 
 BwdPlan plan_bwd(const sp_desc_t* d) {
     BwdPlan p{};
-    const int64_t R = shard_rows(d);
-    const int64_t nchunk = d->H / elems_per_chunk(d->dtype);
+    const int64_t R = shard_rows(d), H = d->H;
+    const int64_t nchunk = H / elems_per_chunk(d->dtype);
+    p.nacc = d->norm == SP_LAYERNORM ? 2 : 1;
     p.variant = pick_bwd_variant(nchunk, SP_BWD_VARIANT);
     if (p.variant < 0) return p;  // unreachable for a validated descriptor
     const BwdVariant v = kBwdVariants[p.variant];
     const int step = v.rg * v.pf;  // rows a workgroup takes per step
-    p.block = v.rg * v.tpr;
-    p.nacc = d->norm == SP_LAYERNORM ? 2 : 1;
     int64_t rpb = (R + SP_BWD_TARGET_BLOCKS - 1) / SP_BWD_TARGET_BLOCKS;
     rpb = ((rpb + step - 1) / step) * step;
     if (rpb < step) rpb = step;
+    p.block = v.rg * v.tpr;
     p.rows_per_block = rpb;
     p.blocks = R > 0 ? (R + rpb - 1) / rpb : 0;
-    p.ws_bytes = (size_t)p.blocks * (size_t)p.nacc * (size_t)d->H * sizeof(float);
-    p.lds_bytes = v.rg > 1 ? (size_t)v.rg * (size_t)p.nacc * (size_t)d->H * sizeof(float) : 0;
+    p.ws_bytes = (size_t)p.blocks * (size_t)p.nacc * (size_t)H * sizeof(float);
+    p.lds_bytes = v.rg > 1 ? (size_t)v.rg * (size_t)p.nacc * (size_t)H * sizeof(float) : 0;
     return p;
 }
 
@@ -950,10 +952,11 @@ extern "C" int sp_region_traffic_bytes(const sp_desc_t* d, uint64_t* fwd_bytes, 
     const uint64_t ln = d->norm == SP_LAYERNORM ? 1 : 0;
     const uint64_t stats = R * 4 * (1 + ln);    // rstd (+ mean)
     const uint64_t params = H * 4 * (1 + ln);   // gamma (+ beta) / dgamma (+ dbeta)
+    const uint64_t mask = (d->flags & SP_FLAG_RECOMPUTE_MASK) ? 0 : N;
     // fwd: T partial slabs + residual in; h, y, mask, stats out; gamma/beta in
-    *fwd_bytes = T * N * e + N * e + N * e + N * e + N + stats + params;
+    *fwd_bytes = T * N * e + N * e + N * e + N * e + mask + stats + params;
     // bwd: dY, h, mask, stats, gamma in; d_residual, dP, dgamma/dbeta out
-    *bwd_bytes = N * e + N * e + N + stats + H * 4 + N * e + N * e + params;
+    *bwd_bytes = N * e + N * e + mask + stats + H * 4 + N * e + N * e + params;
     return SP_OK;
 }
 
@@ -973,8 +976,10 @@ extern "C" int sp_region_fwd(const sp_desc_t* d, const void* const* P, const voi
     const int64_t base = (int64_t)d->j * N;
     // [H] parameters are always required; shard-sized tensors only when the shard has rows
     if (!gamma || ln != (beta != nullptr)) return SP_EINVAL;
+    const bool regen = (d->flags & SP_FLAG_RECOMPUTE_MASK) != 0;
+    if (regen && mask_out) return SP_EINVAL;
     if (R > 0) {
-        if (!P || !residual || !h_out || !y_out || !mask_out || !rstd_out) return SP_EINVAL;
+        if (!P || !residual || !h_out || !y_out || (!regen && !mask_out) || !rstd_out) return SP_EINVAL;
         if (ln != (mean_out != nullptr)) return SP_EINVAL;
         for (int t = 0; t < d->T; ++t)
             if (!P[t]) return SP_EINVAL;
@@ -1000,7 +1005,7 @@ extern "C" int sp_region_fwd(const sp_desc_t* d, const void* const* P, const voi
     int nout = 0;
     outs[nout++] = span(h_out, N * eb);
     outs[nout++] = span(y_out, N * eb);
-    outs[nout++] = span(mask_out, N);
+    if (mask_out) outs[nout++] = span(mask_out, N);
     outs[nout++] = span(rstd_out, R * 4);
     if (mean_out) outs[nout++] = span(mean_out, R * 4);
     if (any_overlap(outs, nout, ins, nin)) return SP_EINVAL;
@@ -1022,7 +1027,7 @@ extern "C" int sp_region_fwd(const sp_desc_t* d, const void* const* P, const voi
     a.nchunk = (int32_t)(H / elems_per_chunk(d->dtype));
     a.T = d->T;
     a.norm = d->norm;
-    a.thr = (uint32_t)floor((double)d->p * 4294967296.0);
+    a.thr = keep_threshold(d->p);
     a.key0 = (uint32_t)d->seed;
     a.key1 = (uint32_t)(d->seed >> 32);
     a.scale = (float)(1.0 / (1.0 - (double)d->p));
@@ -1052,8 +1057,10 @@ extern "C" int sp_region_bwd(const sp_desc_t* d, const void* dY, const void* h, 
     const bool ln = d->norm == SP_LAYERNORM;
     // [H] tensors are always required; shard-sized tensors only when the shard has rows
     if (!gamma || !dgamma || ln != (dbeta != nullptr)) return SP_EINVAL;
+    const bool regen = (d->flags & SP_FLAG_RECOMPUTE_MASK) != 0;
+    if (regen && mask) return SP_EINVAL;
     if (shard_rows(d) > 0) {
-        if (!dY || !h || !mask || !rstd || !d_residual || !dP) return SP_EINVAL;
+        if (!dY || !h || (!regen && !mask) || !rstd || !d_residual || !dP) return SP_EINVAL;
         if (ln != (mean != nullptr)) return SP_EINVAL;
     } else if (!ln && mean) {
         return SP_EINVAL;
@@ -1071,7 +1078,7 @@ extern "C" int sp_region_bwd(const sp_desc_t* d, const void* dY, const void* h, 
     int nin = 0;
     ins[nin++] = span(dY, N * eb);
     ins[nin++] = span(h, N * eb);
-    ins[nin++] = span(mask, N);
+    if (mask) ins[nin++] = span(mask, N);
     ins[nin++] = span(rstd, R * 4);
     ins[nin++] = span(gamma, H * 4);
     if (mean) ins[nin++] = span(mean, R * 4);
@@ -1105,13 +1112,17 @@ extern "C" int sp_region_bwd(const sp_desc_t* d, const void* dY, const void* h, 
     a.nacc = plan.nacc;
     a.scale = (float)(1.0 / (1.0 - (double)d->p));
     a.inv_h = (float)(1.0 / (double)H);
+    a.base = (uint64_t)((int64_t)d->j * N);
+    a.thr = keep_threshold(d->p);
+    a.key0 = (uint32_t)d->seed;
+    a.key1 = (uint32_t)(d->seed >> 32);
 
     if (plan.variant < 0) return SP_ESHAPE;
     if (plan.blocks > INT32_MAX) return SP_ESHAPE;
     (void)hipGetLastError();
     if (plan.blocks > 0) {
-        const BwdKernel k =
-            kBwd[d->dtype == SP_BF16 ? 1 : 0][d->norm == SP_LAYERNORM ? 1 : 0][dR ? 1 : 0][plan.variant];
+        const BwdKernel k = kBwd[d->dtype == SP_BF16 ? 1 : 0][d->norm == SP_LAYERNORM ? 1 : 0][dR ? 1 : 0]
+                                [regen ? 1 : 0][plan.variant];
         hipLaunchKernelGGL(k, dim3((unsigned)plan.blocks), dim3(plan.block),
                            (unsigned)plan.lds_bytes, (hipStream_t)stream, a);
         const hipError_t e = hipGetLastError();
