@@ -144,7 +144,13 @@ int sp_region_fwd(const sp_desc_t* d, const void* const* P, const void* residual
  * dgamma    [H] fp32, overwritten.  dbeta: [H] fp32 for LayerNorm, NULL for RMSNorm.
  * workspace device scratch of at least sp_region_bwd_workspace_size(d) bytes,
  *           16-byte aligned; contents on entry are ignored.  Calls that share a
- *           workspace must be ordered on one stream.
+ *           workspace must be ordered on one stream.  When that size is 0 the
+ *           workspace is not touched and may be NULL.
+ *
+ * dgamma / dbeta are fp32 sums in a fixed order, so repeated calls give the same
+ * bits.  Two schedules exist, chosen from the shape: per-workgroup partial rows
+ * in the workspace summed by a second kernel, or (short shards) workgroups that
+ * each sum a strip of columns over all rows inside the one launch (no workspace).
  */
 int sp_region_bwd(const sp_desc_t* d, const void* dY, const void* h, const uint8_t* mask,
                   const float* mean, const float* rstd, const float* gamma,
@@ -152,7 +158,8 @@ int sp_region_bwd(const sp_desc_t* d, const void* dY, const void* h, const uint8
                   void* d_residual, void* dP, float* dgamma, float* dbeta,
                   void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace sp_region_bwd needs for this descriptor (0 on a bad one). */
+/* Bytes of workspace sp_region_bwd needs for this descriptor: 0 when it needs
+ * none (then the workspace may be NULL) and on a bad descriptor. */
 size_t sp_region_bwd_workspace_size(const sp_desc_t* d);
 
 /*

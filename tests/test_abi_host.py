@@ -189,8 +189,15 @@ def test_fwd_empty_shard_is_a_noop(lib):
     assert fwd_call(good_desc(B=0)) == 0
 
 
+def rows_desc(**kw):
+    """A shard long enough for the partial-row schedule (it needs a workspace)."""
+    base = dict(S=2048, B=1, H=256, T=4, j=1)
+    base.update(kw)
+    return good_desc(**base)
+
+
 def test_bwd_errors(lib):
-    d = good_desc()
+    d = rows_desc()
     need = sp.sp_region_bwd_workspace_size(d)
     assert need > 0
     assert bwd_call(d, ws_bytes=need - 1) == -6
@@ -226,7 +233,30 @@ def test_traffic_bytes_follow_the_accounting(lib):
 
 
 def test_workspace_size_scales_with_norm(lib):
-    rms = sp.sp_region_bwd_workspace_size(good_desc(norm="rms"))
-    ln = sp.sp_region_bwd_workspace_size(good_desc(norm="ln"))
+    rms = sp.sp_region_bwd_workspace_size(rows_desc(norm="rms"))
+    ln = sp.sp_region_bwd_workspace_size(rows_desc(norm="ln"))
     assert ln == 2 * rms and rms % 16 == 0
     assert sp.sp_region_bwd_workspace_size(good_desc(S=0)) == 0
+
+
+@pytest.mark.parametrize("shape,uses_workspace", [
+    # (S, B, H, T, dtype, norm): short shards sum dgamma by columns (no workspace)
+    ((4096, 1, 4096, 8, "bf16", "ln"), False),   # the LayerNorm T=8 shard, 512 rows
+    ((400, 3, 2056, 4, "bf16", "ln"), False),    # 300 rows, a ragged last strip
+    ((40, 5, 2000, 2, "f32", "ln"), False),
+    ((256, 1, 64, 2, "f32", "rms"), False),
+    ((8192, 2, 8192, 8, "bf16", "rms"), True),   # 2048 rows of 8192
+    ((2048, 2, 768, 2, "bf16", "rms"), True),    # 2048 rows of 768
+    ((32768, 1, 8192, 8, "bf16", "rms"), True),
+    ((4096, 4, 128, 4, "bf16", "ln"), True),     # 4096 short rows
+])
+def test_backward_schedule_by_shape(lib, shape, uses_workspace):
+    """Both dgamma schedules are exercised by the GPU parity shapes listed here."""
+    S, B, H, T, dtype, norm = shape
+    d = sp.make_desc(S, B, H, T, 1, dtype, norm)
+    need = sp.sp_region_bwd_workspace_size(d)
+    assert (need > 0) == uses_workspace
+    if not uses_workspace:
+        # no workspace needed: validation still catches every other error
+        assert bwd_call(d, workspace=None, ws_bytes=0, dY=None) == -1
+        assert bwd_call(d, workspace=None, ws_bytes=0, dgamma=fake(2)) == -1  # dgamma over h

@@ -394,40 +394,44 @@ def test_gpu_argument_errors_leave_outputs_untouched():
     assert bool((h == 3).all()) and bool((y == 3).all()) and bool((m == 3).all())
 
 
-def test_graph_replays_match_eager():
+@pytest.mark.parametrize("name,j", [("minimind_T2_S2048_B2_H768", 1), ("layernorm_T8_S4096_B1_H4096", 3)])
+def test_graph_replays_match_eager(name, j):
     """The library enqueues kernels only (no memset, no allocation), so a HIP
     graph of forward + backward replays to the eager results every time, with
-    the program's own eager work between replays."""
-    print("\n[case] HIP graph capture of forward + backward, three replays", flush=True)
-    w = W.WORKLOADS["minimind_T2_S2048_B2_H768"]
+    the program's own eager work between replays.  The two shards use the two
+    dgamma schedules (partial rows + finish kernel; column workgroups)."""
+    print(f"\n[case] {name} shard {j}: HIP graph capture of forward + backward, three replays",
+          flush=True)
+    w = W.WORKLOADS[name]
     c = Case(w, "cpu")
-    j = 1
     d = gdesc(w, j)
+    ln = w.norm == "ln"
     f = gpu_fwd(c, j)
     b = gpu_bwd(c, j, f)
     torch.cuda.synchronize()
-    ref = {**{k: f[k].clone() for k in ("h", "y", "mask", "rstd")},
-           **{k: b[k].clone() for k in ("d_res", "dP", "dgamma")}}
+    fk = ("h", "y", "mask", "rstd") + (("mean",) if ln else ())
+    bk = ("d_res", "dP", "dgamma") + (("dbeta",) if ln else ())
+    ref = {**{k: f[k].clone() for k in fk}, **{k: b[k].clone() for k in bk}}
     ws = torch.empty(max(16, sp.sp_region_bwd_workspace_size(d)), dtype=torch.uint8, device="cuda")
     s = torch.cuda.Stream()
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
-        rc1 = sp.sp_region_fwd(d, c.P, c.shard(c.res, j), c.gamma, None, f["h"], f["y"], f["mask"],
-                               None, f["rstd"], stream=s)
-        rc2 = sp.sp_region_bwd(d, c.shard(c.dY, j), f["h"], f["mask"], None, f["rstd"], c.gamma, None,
-                               b["d_res"], b["dP"], b["dgamma"], None, ws, ws.numel(), stream=s)
+        rc1 = sp.sp_region_fwd(d, c.P, c.shard(c.res, j), c.gamma, c.beta, f["h"], f["y"], f["mask"],
+                               f["mean"], f["rstd"], stream=s)
+        rc2 = sp.sp_region_bwd(d, c.shard(c.dY, j), f["h"], f["mask"], f["mean"], f["rstd"], c.gamma,
+                               None, b["d_res"], b["dP"], b["dgamma"], b["dbeta"], ws, ws.numel(),
+                               stream=s)
     assert rc1 == 0 and rc2 == 0
     for rep in range(3):
-        for t in (f["h"], f["y"], f["rstd"], b["d_res"], b["dP"], b["dgamma"]):
-            t.zero_()
-        other = gpu_fwd(c, 0)  # unrelated eager work between replays
+        for k in fk + bk:
+            (f if k in fk else b)[k].zero_()
+        other = gpu_fwd(c, (j + 1) % w.T)  # unrelated eager work between replays
         torch.cuda.synchronize()
         with torch.cuda.stream(s):
             g.replay()
         torch.cuda.synchronize()
-        got = {**{k: f[k] for k in ("h", "y", "mask", "rstd")},
-               **{k: b[k] for k in ("d_res", "dP", "dgamma")}}
+        got = {**{k: f[k] for k in fk}, **{k: b[k] for k in bk}}
         for k in ref:
             assert torch.equal(ref[k], got[k]), (rep, k)
         del other

@@ -107,6 +107,18 @@ __device__ __forceinline__ u32x4 ld16(const void* base, int64_t byte_off) {
     return *p;
 #endif
 }
+// Loads of the backward's column workgroups (a second read of dY and h).
+#ifndef SP_COL_NT
+#define SP_COL_NT 1
+#endif
+__device__ __forceinline__ u32x4 ld16_col(const void* base, int64_t byte_off) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(base) + byte_off);
+#if SP_COL_NT
+    return __builtin_nontemporal_load(p);
+#else
+    return *p;
+#endif
+}
 __device__ __forceinline__ void st16(void* base, int64_t byte_off, u32x4 v) {
     u32x4* p = reinterpret_cast<u32x4*>(reinterpret_cast<char*>(base) + byte_off);
 #if SP_NT_STORES
@@ -190,7 +202,9 @@ __device__ __forceinline__ float lanes_sum(float v) {
 
 // Sum NV values over the TPR lanes of each row group of a BLOCK-thread block.
 // Must be reached by every thread of the block (it may synchronise).
-template <int TPR, int BLOCK, int NV>
+// REUSE: the LDS words are written again later in the kernel, so wait for every
+// wavefront to have read them before returning.
+template <int TPR, int BLOCK, int NV, bool REUSE = true>
 __device__ __forceinline__ void group_sum(float (&v)[NV]) {
 #pragma unroll
     for (int i = 0; i < NV; ++i) v[i] = lanes_sum<TPR>(v[i]);
@@ -213,7 +227,7 @@ __device__ __forceinline__ void group_sum(float (&v)[NV]) {
             for (int q = 1; q < NW; ++q) s += red[(rg * NW + q) * NV + i];
             v[i] = s;
         }
-        __syncthreads();
+        if constexpr (REUSE) __syncthreads();
     }
 }
 
@@ -414,7 +428,7 @@ __global__ __launch_bounds__(BLOCK) void sp_fwd_kernel(const FwdArgs a) {
                     const float dlt = hv[k][e] - mu;
                     q[0] += dlt * dlt;
                 }
-        group_sum<TPR, BLOCK, 1>(q);
+        group_sum<TPR, BLOCK, 1, false>(q);
         rs = rsqrtf(q[0] * a.inv_h + a.eps);
     } else {
         float q[1] = {0.0f};
@@ -423,7 +437,7 @@ __global__ __launch_bounds__(BLOCK) void sp_fwd_kernel(const FwdArgs a) {
             if (ok[k])
 #pragma unroll
                 for (int e = 0; e < E; ++e) q[0] += hv[k][e] * hv[k][e];
-        group_sum<TPR, BLOCK, 1>(q);
+        group_sum<TPR, BLOCK, 1, false>(q);
         rs = rsqrtf(q[0] * a.inv_h + a.eps);
     }
 
@@ -460,6 +474,8 @@ struct BwdArgs {
     void* dres;
     void* dP;
     float* ws;            // [G][nacc][H] fp32 partial sums of dgamma (, dbeta)
+    float* dgamma;        // [H] outputs, written directly by the column workgroups
+    float* dbeta;
     uint64_t base;        // global index of the shard's first element (mask regeneration)
     uint32_t thr, key0, key1;
     int64_t R;
@@ -468,6 +484,7 @@ struct BwdArgs {
     int32_t nchunk;
     int32_t norm;
     int32_t nacc;         // 1 (RMSNorm) or 2 (LayerNorm)
+    int32_t col_blocks;   // leading workgroups that sum dgamma / dbeta by columns (0 = partial rows)
     float scale;
     float inv_h;
 };
@@ -514,6 +531,104 @@ __device__ __forceinline__ void bwd_load_step(const BwdArgs& a, int64_t row0, in
     }
 }
 
+// dgamma / dbeta by columns.  Workgroup `strip` owns kSeg adjacent 16-byte
+// chunks (128 bytes of every row, lanes kSeg apart share a chunk) and sums
+// dY * xhat (and dY) over all R rows of the shard: its BLOCK / kSeg row offsets
+// each take every (BLOCK / kSeg)-th row in ascending order, then the offsets
+// are added in a fixed tree (lane butterfly inside a wavefront, wavefronts in
+// order through LDS).  Needs no partial rows and no second launch, at the cost
+// of reading dY and h a second time.
+#ifndef SP_COL_BATCH
+#define SP_COL_BATCH 8
+#endif
+constexpr int kColBatch = SP_COL_BATCH;
+#ifndef SP_COL_SEG
+#define SP_COL_SEG 8
+#endif
+constexpr int kSeg = SP_COL_SEG;  // lanes per row segment (16 bytes each)
+
+template <int DT, bool LN, int BLOCK>
+__device__ __forceinline__ void bwd_columns(const BwdArgs& a, int strip) {
+    using A = Act<DT>;
+    constexpr int E = A::E;
+    constexpr int EB = A::kBytes;
+    constexpr int NACC = LN ? 2 : 1;
+    constexpr int kRO = BLOCK / kSeg;  // row offsets
+    constexpr int kB = kColBatch;      // steps whose loads are in flight together
+    constexpr int NW = BLOCK / kWave;
+    __shared__ float cred[NW][NACC][kSeg * E];
+
+    const int tid = threadIdx.x;
+    const int ch = tid % kSeg;
+    const int ro = tid / kSeg;
+    const int c = strip * kSeg + ch;
+    const bool cok = c < a.nchunk;
+    const int col = (cok ? c : a.nchunk - 1) * E;
+    float dg[E], db[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        dg[e] = 0.0f;
+        db[e] = 0.0f;
+    }
+    for (int64_t r0 = 0; r0 < a.R; r0 += (int64_t)kRO * kB) {
+        u32x4 dy[kB], hh[kB];
+        float mu[kB], rs[kB];
+        bool rok[kB];
+#pragma unroll
+        for (int b = 0; b < kB; ++b) {
+            const int64_t row = r0 + (int64_t)b * kRO + ro;
+            rok[b] = row < a.R;
+            const int64_t rr = rok[b] ? row : a.R - 1;
+            const int64_t off = (rr * a.H + col) * EB;
+            dy[b] = ld16_col(a.dY, off);
+            hh[b] = ld16_col(a.h, off);
+            rs[b] = a.rstd[rr];
+            mu[b] = LN ? a.mean[rr] : 0.0f;
+        }
+#pragma unroll
+        for (int b = 0; b < kB; ++b) {
+            float dyv[E], hv[E];
+            A::unpack(dy[b], dyv);
+            A::unpack(hh[b], hv);
+            if (rok[b]) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float x = (hv[e] - mu[b]) * rs[b];
+                    dg[e] += dyv[e] * x;
+                    if constexpr (LN) db[e] += dyv[e];
+                }
+            }
+        }
+    }
+    // the row offsets inside a wavefront (lanes kSeg, 2 kSeg, ... apart), then the wavefronts
+#pragma unroll
+    for (int m = kSeg; m < kWave; m *= 2) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            dg[e] += __shfl_xor(dg[e], m);
+            if constexpr (LN) db[e] += __shfl_xor(db[e], m);
+        }
+    }
+    const int w = tid / kWave;
+    if (tid % kWave < kSeg) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            cred[w][0][ch * E + e] = dg[e];
+            if constexpr (LN) cred[w][1][ch * E + e] = db[e];
+        }
+    }
+    __syncthreads();
+    if (tid < NACC * kSeg * E) {
+        const int acc = tid / (kSeg * E);
+        const int cc = tid % (kSeg * E);
+        float v = cred[0][acc][cc];
+#pragma unroll
+        for (int q = 1; q < NW; ++q) v += cred[q][acc][cc];
+        const int gcol = strip * kSeg * E + cc;
+        if (gcol < a.H) (acc == 0 ? a.dgamma : a.dbeta)[gcol] = v;
+    }
+}
+
 // A workgroup holds RG row groups of TPR lanes and walks a tile of
 // rows_per_block rows.  In each step every row group takes PF rows whose loads
 // are all in flight together, reduces the PF rows' two sums in one pass, then
@@ -536,7 +651,12 @@ __global__ __launch_bounds__(RG* TPR) void sp_bwd_kernel(const BwdArgs a) {
     const int tid = threadIdx.x;
     const int rg = tid / TPR;
     const int l = tid % TPR;
-    const int64_t row_begin = (int64_t)blockIdx.x * a.rows_per_block;
+    if ((int)blockIdx.x < a.col_blocks) {  // grid-uniform choice per workgroup
+        bwd_columns<DT, LN, BLOCK>(a, (int)blockIdx.x);
+        return;
+    }
+    const bool partial_rows = a.col_blocks == 0;
+    const int64_t row_begin = (int64_t)(blockIdx.x - a.col_blocks) * a.rows_per_block;
     const int64_t row_end = min(row_begin + a.rows_per_block, a.R);
     const int iters = (int)((a.rows_per_block + STEP - 1) / STEP);  // uniform over the grid
 
@@ -589,7 +709,7 @@ __global__ __launch_bounds__(RG* TPR) void sp_bwd_kernel(const BwdArgs a) {
                         const float g = dyv[e] * gam[k][e];
                         if constexpr (LN) s[2 * p] += g;
                         s[2 * p + 1] += g * x;
-                        if (row_ok) {
+                        if (row_ok && partial_rows) {
                             dg[k][e] += dyv[e] * x;
                             if constexpr (LN) db[k][e] += dyv[e];
                         }
@@ -644,7 +764,8 @@ __global__ __launch_bounds__(RG* TPR) void sp_bwd_kernel(const BwdArgs a) {
     }
 
     // ---- this workgroup's partial dgamma / dbeta row ----
-    float* out = a.ws + (int64_t)blockIdx.x * NACC * a.H;
+    if (!partial_rows) return;
+    float* out = a.ws + (int64_t)(blockIdx.x - a.col_blocks) * NACC * a.H;
     if constexpr (RG == 1) {
 #pragma unroll
         for (int k = 0; k < CPT; ++k) {
@@ -735,14 +856,13 @@ __global__ __launch_bounds__(kFinGroups* kFinSlices) void sp_dgamma_finish_kerne
 struct Layout {
     int tpr, cpt;
 };
-// Entries 0..kNumDefault-1 are the default choices, in increasing capacity
-// (tpr * cpt chunks); the rest are alternatives kept for tuning.
+// In increasing capacity (tpr * cpt chunks); the first that holds the row is used.
 constexpr Layout kLayouts[] = {
-    {16, 1},  {32, 1},  {64, 1},  {32, 3},   {64, 2},    {64, 3},  {64, 4},  {512, 1},  {512, 2},
-    {512, 4}, {1024, 4}, {1024, 8}, {128, 4}, {256, 2},  {256, 4}, {1024, 1}, {128, 8},
+    {16, 1},  {32, 1},  {64, 1},  {32, 3},   {64, 2},    {64, 3},
+    {64, 4},  {512, 1}, {512, 2}, {512, 4}, {1024, 4}, {1024, 8},
 };
 constexpr int kNumLayouts = sizeof(kLayouts) / sizeof(kLayouts[0]);
-constexpr int kNumDefault = 12;
+constexpr int kNumDefault = kNumLayouts;
 #ifndef SP_SUBWAVE_BLOCK
 #define SP_SUBWAVE_BLOCK 256
 #endif
@@ -779,8 +899,7 @@ typedef void (*BwdKernel)(BwdArgs);
     X(16, 1, __VA_ARGS__), X(32, 1, __VA_ARGS__), X(64, 1, __VA_ARGS__), X(32, 3, __VA_ARGS__),   \
         X(64, 2, __VA_ARGS__), X(64, 3, __VA_ARGS__), X(64, 4, __VA_ARGS__),                      \
         X(512, 1, __VA_ARGS__), X(512, 2, __VA_ARGS__), X(512, 4, __VA_ARGS__),                   \
-        X(1024, 4, __VA_ARGS__), X(1024, 8, __VA_ARGS__), X(128, 4, __VA_ARGS__),                 \
-        X(256, 2, __VA_ARGS__), X(256, 4, __VA_ARGS__), X(1024, 1, __VA_ARGS__), X(128, 8, __VA_ARGS__)
+        X(1024, 4, __VA_ARGS__), X(1024, 8, __VA_ARGS__)
 
 #define SP_FWD_ENTRY(TPR, CPT, DT, TT) &sp_fwd_kernel<DT, TT, TPR, CPT, block_of(TPR)>
 #define SP_BWD_LIST(X, ...)                                                                      \
@@ -895,7 +1014,27 @@ struct BwdPlan {
     int nacc;
     size_t ws_bytes;
     size_t lds_bytes;
+    int64_t col_blocks;  // > 0: dgamma / dbeta by column workgroups, no workspace, no finish
 };
+
+// dgamma / dbeta strategy: 0 = by estimated bytes, 1 = partial rows + finish
+// kernel, 2 = column workgroups.
+#ifndef SP_BWD_DG
+#define SP_BWD_DG 0
+#endif
+// The finish launch costs about as much time as moving this many bytes.
+constexpr int64_t kFinishLaunchBytes = (int64_t)16 << 20;
+
+// Column workgroups read dY and h a second time (2 R H e bytes) but need no
+// partial rows (2 G nacc H 4 bytes written and read back) and no second launch.
+// They are used only where each of their lanes issues all of its loads in one
+// batch: a longer column walk becomes the critical path of the launch.
+bool use_columns(int64_t R, int64_t H, int eb, int64_t G, int nacc, int block) {
+    if (SP_BWD_DG == 1 || R == 0) return false;
+    if (SP_BWD_DG == 2) return true;
+    if (R > (int64_t)(block / kSeg) * kColBatch) return false;
+    return 2 * R * H * eb <= 2 * G * nacc * H * 4 + kFinishLaunchBytes;
+}
 
 BwdPlan plan_bwd(const sp_desc_t* d) {
     BwdPlan p{};
@@ -912,6 +1051,10 @@ BwdPlan plan_bwd(const sp_desc_t* d) {
     p.block = v.rg * v.tpr;
     p.rows_per_block = rpb;
     p.blocks = R > 0 ? (R + rpb - 1) / rpb : 0;
+    if (use_columns(R, H, elem_bytes(d->dtype), p.blocks, p.nacc, p.block)) {
+        p.col_blocks = (nchunk + kSeg - 1) / kSeg;
+        return p;
+    }
     p.ws_bytes = (size_t)p.blocks * (size_t)p.nacc * (size_t)H * sizeof(float);
     p.lds_bytes = v.rg > 1 ? (size_t)v.rg * (size_t)p.nacc * (size_t)H * sizeof(float) : 0;
     return p;
@@ -1104,6 +1247,9 @@ extern "C" int sp_region_bwd(const sp_desc_t* d, const void* dY, const void* h, 
     a.dres = d_residual;
     a.dP = dP;
     a.ws = (float*)workspace;
+    a.dgamma = dgamma;
+    a.dbeta = dbeta;
+    a.col_blocks = (int32_t)plan.col_blocks;
     a.R = R;
     a.rows_per_block = plan.rows_per_block;
     a.H = (int32_t)H;
@@ -1118,16 +1264,17 @@ extern "C" int sp_region_bwd(const sp_desc_t* d, const void* dY, const void* h, 
     a.key1 = (uint32_t)(d->seed >> 32);
 
     if (plan.variant < 0) return SP_ESHAPE;
-    if (plan.blocks > INT32_MAX) return SP_ESHAPE;
+    if (plan.blocks + plan.col_blocks > INT32_MAX) return SP_ESHAPE;
     (void)hipGetLastError();
     if (plan.blocks > 0) {
         const BwdKernel k = kBwd[d->dtype == SP_BF16 ? 1 : 0][d->norm == SP_LAYERNORM ? 1 : 0][dR ? 1 : 0]
                                 [regen ? 1 : 0][plan.variant];
-        hipLaunchKernelGGL(k, dim3((unsigned)plan.blocks), dim3(plan.block),
+        hipLaunchKernelGGL(k, dim3((unsigned)(plan.col_blocks + plan.blocks)), dim3(plan.block),
                            (unsigned)plan.lds_bytes, (hipStream_t)stream, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return record_hip(e);
     }
+    if (plan.col_blocks > 0) return SP_OK;  // the column workgroups wrote dgamma / dbeta
     const int ncols = plan.nacc * (int)H;
     const unsigned fin_grid = (unsigned)((ncols / 4 + kFinGroups - 1) / kFinGroups);
     hipLaunchKernelGGL(sp_dgamma_finish_kernel, dim3(fin_grid), dim3(kFinGroups * kFinSlices), 0,
