@@ -107,17 +107,23 @@ __device__ __forceinline__ u32x4 ld16(const void* base, int64_t byte_off) {
     return *p;
 #endif
 }
-// Loads of the backward's column workgroups (a second read of dY and h).
+// dY and h in the backward.  Under the column schedule they are read twice (by
+// the row and by the column workgroups), so both reads use ordinary loads,
+// which leave the lines in the caches for the other read; otherwise the row
+// workgroups stream them like every other tensor.
 #ifndef SP_COL_NT
-#define SP_COL_NT 1
+#define SP_COL_NT 0
 #endif
-__device__ __forceinline__ u32x4 ld16_col(const void* base, int64_t byte_off) {
+template <bool NT>
+__device__ __forceinline__ u32x4 ld16_policy(const void* base, int64_t byte_off) {
     const u32x4* p = reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(base) + byte_off);
-#if SP_COL_NT
-    return __builtin_nontemporal_load(p);
-#else
-    return *p;
-#endif
+    if constexpr (NT)
+        return __builtin_nontemporal_load(p);
+    else
+        return *p;
+}
+__device__ __forceinline__ u32x4 ld16_col(const void* base, int64_t byte_off) {
+    return ld16_policy<SP_COL_NT != 0>(base, byte_off);
 }
 __device__ __forceinline__ void st16(void* base, int64_t byte_off, u32x4 v) {
     u32x4* p = reinterpret_cast<u32x4*>(reinterpret_cast<char*>(base) + byte_off);
@@ -499,7 +505,7 @@ struct BwdRow {
     float mu, rs;
 };
 
-template <int DT, bool LN, int CPT, bool HAS_DR, bool REGEN>
+template <int DT, bool LN, int CPT, bool HAS_DR, bool REGEN, bool NT>
 __device__ __forceinline__ void bwd_load(const BwdArgs& a, int64_t rowc, const int (&col)[CPT],
                                          BwdRow<CPT, Act<DT>::E>& b) {
     using A = Act<DT>;
@@ -509,8 +515,8 @@ __device__ __forceinline__ void bwd_load(const BwdArgs& a, int64_t rowc, const i
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
         const int64_t idx = row_elem + col[k];
-        b.dy[k] = ld16(a.dY, idx * EB);
-        b.hh[k] = ld16(a.h, idx * EB);
+        b.dy[k] = ld16_policy<NT && SP_NT_LOADS>(a.dY, idx * EB);
+        b.hh[k] = ld16_policy<NT && SP_NT_LOADS>(a.h, idx * EB);
         if constexpr (HAS_DR) b.dr[k] = ld16(a.dR, idx * EB);
         if constexpr (!REGEN) b.m[k] = *reinterpret_cast<const typename MaskWord<E>::type*>(a.mask + idx);
     }
@@ -520,14 +526,14 @@ __device__ __forceinline__ void bwd_load(const BwdArgs& a, int64_t rowc, const i
 
 // The PF rows one row group takes in step `it` (rows past the tile's end are
 // loaded from a valid row and never stored).
-template <int DT, bool LN, int CPT, int PF, bool HAS_DR, bool REGEN>
+template <int DT, bool LN, int CPT, int PF, bool HAS_DR, bool REGEN, bool NT>
 __device__ __forceinline__ void bwd_load_step(const BwdArgs& a, int64_t row0, int64_t row_end,
                                               const int (&col)[CPT],
                                               BwdRow<CPT, Act<DT>::E> (&rows)[PF]) {
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
         const int64_t r = row0 + p;
-        bwd_load<DT, LN, CPT, HAS_DR, REGEN>(a, r < row_end ? r : a.R - 1, col, rows[p]);
+        bwd_load<DT, LN, CPT, HAS_DR, REGEN, NT>(a, r < row_end ? r : a.R - 1, col, rows[p]);
     }
 }
 
@@ -636,7 +642,7 @@ __device__ __forceinline__ void bwd_columns(const BwdArgs& a, int strip) {
 // this step is computed.  dgamma (and dbeta) accumulate in registers and each
 // workgroup writes one partial row.  With REGEN the keep flags are generated
 // again from (seed, global index) instead of read from a mask tensor.
-template <int DT, int NORM, int TPR, int CPT, int RG, int PF, bool PIPE, bool HAS_DR, bool REGEN>
+template <int DT, int NORM, int TPR, int CPT, int RG, int PF, bool PIPE, bool HAS_DR, bool REGEN, bool COLS>
 __global__ __launch_bounds__(RG* TPR) void sp_bwd_kernel(const BwdArgs a) {
     using A = Act<DT>;
     constexpr bool LN = NORM == SP_LAYERNORM;
@@ -651,11 +657,13 @@ __global__ __launch_bounds__(RG* TPR) void sp_bwd_kernel(const BwdArgs a) {
     const int tid = threadIdx.x;
     const int rg = tid / TPR;
     const int l = tid % TPR;
-    if ((int)blockIdx.x < a.col_blocks) {  // grid-uniform choice per workgroup
-        bwd_columns<DT, LN, BLOCK>(a, (int)blockIdx.x);
-        return;
+    if constexpr (COLS) {
+        if ((int)blockIdx.x < a.col_blocks) {  // grid-uniform choice per workgroup
+            bwd_columns<DT, LN, BLOCK>(a, (int)blockIdx.x);
+            return;
+        }
     }
-    const bool partial_rows = a.col_blocks == 0;
+    constexpr bool partial_rows = !COLS;
     const int64_t row_begin = (int64_t)(blockIdx.x - a.col_blocks) * a.rows_per_block;
     const int64_t row_end = min(row_begin + a.rows_per_block, a.R);
     const int iters = (int)((a.rows_per_block + STEP - 1) / STEP);  // uniform over the grid
@@ -682,13 +690,17 @@ __global__ __launch_bounds__(RG* TPR) void sp_bwd_kernel(const BwdArgs a) {
     }
 
     BwdRow<CPT, E> rows[PF];
-    bwd_load_step<DT, LN, CPT, PF, HAS_DR, REGEN>(a, row_begin + (int64_t)rg * PF, row_end, col, rows);
+    // streaming loads unless the column workgroups read dY and h again
+    auto load_step = [&](int64_t r0, BwdRow<CPT, E>(&dst)[PF]) {
+        bwd_load_step<DT, LN, CPT, PF, HAS_DR, REGEN, !COLS>(a, r0, row_end, col, dst);
+    };
+    load_step(row_begin + (int64_t)rg * PF, rows);
     for (int it = 0; it < iters; ++it) {
         const int64_t row0 = row_begin + (int64_t)it * STEP + (int64_t)rg * PF;
         BwdRow<CPT, E> nxt[PIPE ? PF : 1];
         if constexpr (PIPE) {
             if (it + 1 < iters)
-                bwd_load_step<DT, LN, CPT, PF, HAS_DR, REGEN>(a, row0 + STEP, row_end, col, nxt);
+                load_step(row0 + STEP, nxt);
         }
         // pass 1: the two row sums of every row, and the dgamma / dbeta terms
         float s[2 * PF];
@@ -758,13 +770,13 @@ __global__ __launch_bounds__(RG* TPR) void sp_bwd_kernel(const BwdArgs a) {
 #pragma unroll
                 for (int p = 0; p < PF; ++p) rows[p] = nxt[p];
             } else {
-                bwd_load_step<DT, LN, CPT, PF, HAS_DR, REGEN>(a, row0 + STEP, row_end, col, rows);
+                load_step(row0 + STEP, rows);
             }
         }
     }
 
     // ---- this workgroup's partial dgamma / dbeta row ----
-    if (!partial_rows) return;
+    if constexpr (COLS) return;
     float* out = a.ws + (int64_t)(blockIdx.x - a.col_blocks) * NACC * a.H;
     if constexpr (RG == 1) {
 #pragma unroll
@@ -909,8 +921,8 @@ typedef void (*BwdKernel)(BwdArgs);
         X(512, 1, 1, 2, 0, __VA_ARGS__), X(512, 2, 1, 2, 0, __VA_ARGS__),                            \
         X(512, 4, 1, 1, 0, __VA_ARGS__), X(1024, 4, 1, 1, 0, __VA_ARGS__),                           \
         X(1024, 8, 1, 1, 0, __VA_ARGS__)
-#define SP_BWD_ENTRY(TPR, CPT, RG, PF, PIPE, DT, NORM, HDR, REGEN) \
-    &sp_bwd_kernel<DT, NORM, TPR, CPT, RG, PF, PIPE != 0, HDR, REGEN>
+#define SP_BWD_ENTRY(TPR, CPT, RG, PF, PIPE, DT, NORM, HDR, REGEN, COLS) \
+    &sp_bwd_kernel<DT, NORM, TPR, CPT, RG, PF, PIPE != 0, HDR, REGEN, COLS>
 
 const FwdKernel kFwdBf16[5][kNumLayouts] = {
     {SP_LAYOUT_LIST(SP_FWD_ENTRY, SP_BF16, 0)}, {SP_LAYOUT_LIST(SP_FWD_ENTRY, SP_BF16, 1)},
@@ -918,13 +930,16 @@ const FwdKernel kFwdBf16[5][kNumLayouts] = {
     {SP_LAYOUT_LIST(SP_FWD_ENTRY, SP_BF16, 8)},
 };
 const FwdKernel kFwdF32[kNumLayouts] = {SP_LAYOUT_LIST(SP_FWD_ENTRY, SP_F32, 0)};
-// [dtype][norm][has dR][mask regenerated][variant]
+// [dtype][norm][has dR][mask regenerated][column schedule][variant]
+#define SP_BWD_BY_REGEN(DT, NORM, HDR, REGEN)                      \
+    {{SP_BWD_LIST(SP_BWD_ENTRY, DT, NORM, HDR, REGEN, false)},     \
+     {SP_BWD_LIST(SP_BWD_ENTRY, DT, NORM, HDR, REGEN, true)}}
 #define SP_BWD_BY_DR(DT, NORM, HDR) \
-    {{SP_BWD_LIST(SP_BWD_ENTRY, DT, NORM, HDR, false)}, {SP_BWD_LIST(SP_BWD_ENTRY, DT, NORM, HDR, true)}}
+    {SP_BWD_BY_REGEN(DT, NORM, HDR, false), SP_BWD_BY_REGEN(DT, NORM, HDR, true)}
 #define SP_BWD_BY_NORM(DT)                                                                       \
     {{SP_BWD_BY_DR(DT, SP_RMSNORM, false), SP_BWD_BY_DR(DT, SP_RMSNORM, true)},                  \
      {SP_BWD_BY_DR(DT, SP_LAYERNORM, false), SP_BWD_BY_DR(DT, SP_LAYERNORM, true)}}
-const BwdKernel kBwd[2][2][2][2][kNumBwdVariants] = {SP_BWD_BY_NORM(SP_F32), SP_BWD_BY_NORM(SP_BF16)};
+const BwdKernel kBwd[2][2][2][2][2][kNumBwdVariants] = {SP_BWD_BY_NORM(SP_F32), SP_BWD_BY_NORM(SP_BF16)};
 
 // ---------------------------------------------------------------------------
 // Host-side validation.
@@ -1268,7 +1283,7 @@ extern "C" int sp_region_bwd(const sp_desc_t* d, const void* dY, const void* h, 
     (void)hipGetLastError();
     if (plan.blocks > 0) {
         const BwdKernel k = kBwd[d->dtype == SP_BF16 ? 1 : 0][d->norm == SP_LAYERNORM ? 1 : 0][dR ? 1 : 0]
-                                [regen ? 1 : 0][plan.variant];
+                                [regen ? 1 : 0][plan.col_blocks > 0 ? 1 : 0][plan.variant];
         hipLaunchKernelGGL(k, dim3((unsigned)(plan.col_blocks + plan.blocks)), dim3(plan.block),
                            (unsigned)plan.lds_bytes, (hipStream_t)stream, a);
         const hipError_t e = hipGetLastError();
