@@ -1,6 +1,8 @@
 """Build the HIP library libsp_region.so for gfx950 (MI355X), in-tree.
 
     python -m transformer_sequence_activation_amd.build [--resource-usage] [-D NAME=VALUE ...]
+    python -m transformer_sequence_activation_amd.build --resource-table 'sp_fwd_kernel<1, 8, 512, 1, 512>;...'
+
 """
 import argparse
 import os
@@ -42,6 +44,44 @@ def build(out=LIB, defines=(), resource_usage=False, verbose=False):
     return out
 
 
+def resource_table(out, kernels=None):
+    """Build `out` with the compiler's kernel-resource remarks and return a text
+    table (kernel, VGPRs, AGPRs, SGPRs, spills, scratch, LDS, waves per SIMD),
+    keeping kernels whose demangled name contains one of `kernels`."""
+    hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
+    tmp = out + ".tmp"
+    cmd = [hipcc, *HIPCC_FLAGS, "-I", INCLUDE, "-Rpass-analysis=kernel-resource-usage", SRC, "-o", tmp]
+    r = subprocess.run(cmd, check=True, capture_output=True, text=True)
+    os.replace(tmp, out)
+    rows, cur = [], None
+    keys = {"VGPRs": "vgpr", "AGPRs": "agpr", "TotalSGPRs": "sgpr", "VGPRs Spill": "vspill",
+            "ScratchSize [bytes/lane]": "scratch", "LDS Size [bytes/block]": "lds",
+            "Occupancy [waves/SIMD]": "occ"}
+    for line in r.stderr.splitlines():
+        if "remark:" not in line:
+            continue
+        body = line.split("remark:", 1)[1].split("[-Rpass", 1)[0].strip()
+        if body.startswith("Function Name:"):
+            cur = {"name": body.split(":", 1)[1].strip()}
+            rows.append(cur)
+        elif cur is not None and ":" in body:
+            k, v = body.split(":", 1)
+            if k.strip() in keys:
+                cur[keys[k.strip()]] = v.strip()
+    names = subprocess.run(["c++filt"], input="\n".join(x["name"] for x in rows), capture_output=True,
+                           text=True).stdout.splitlines()
+    out_lines = [f"{'kernel':<92} {'VGPR':>5} {'AGPR':>5} {'SGPR':>5} {'spill':>5} {'scratch':>7} "
+                 f"{'LDS':>6} {'waves/SIMD':>10}"]
+    for x, n in zip(rows, names):
+        n = n.replace("(anonymous namespace)::", "").replace("void ", "").split("(", 1)[0]
+        if kernels and not any(k in n for k in kernels):
+            continue
+        out_lines.append(f"{n:<92} {x.get('vgpr', '?'):>5} {x.get('agpr', '?'):>5} {x.get('sgpr', '?'):>5} "
+                         f"{x.get('vspill', '?'):>5} {x.get('scratch', '?'):>7} {x.get('lds', '?'):>6} "
+                         f"{x.get('occ', '?'):>10}")
+    return "\n".join(out_lines)
+
+
 def build_probe(out=PROBE, verbose=False):
     """Compile the streaming-bandwidth probe executable; always recompiles."""
     hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
@@ -61,7 +101,13 @@ if __name__ == "__main__":
     ap.add_argument("-D", dest="defines", action="append", default=[])
     ap.add_argument("--resource-usage", action="store_true")
     ap.add_argument("--probe", action="store_true", help="also build the stream_probe executable")
+    ap.add_argument("--resource-table", metavar="KERNELS", default=None,
+                    help="build and print the resource table of the kernels whose names contain one "
+                         "of these ';'-separated substrings ('' = all)")
     args = ap.parse_args()
+    if args.resource_table is not None:
+        print(resource_table(args.out, [k for k in args.resource_table.split(";") if k]))
+        raise SystemExit(0)
     print(build(args.out, args.defines, args.resource_usage, verbose=True))
     if args.probe:
         print(build_probe(verbose=True))
