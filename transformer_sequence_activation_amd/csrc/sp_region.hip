@@ -899,10 +899,20 @@ struct BwdVariant {
 constexpr BwdVariant kBwdVariants[] = {
     {16, 1, 16, 1, 0}, {32, 1, 8, 1, 0}, {64, 1, 4, 1, 0},  {32, 3, 8, 1, 0},  {64, 2, 4, 1, 0},
     {64, 3, 4, 1, 0},  {64, 4, 4, 1, 0}, {512, 1, 1, 2, 0}, {512, 2, 1, 2, 0}, {512, 4, 1, 1, 0},
-    {1024, 4, 1, 1, 0}, {1024, 8, 1, 1, 0},
+    {1024, 4, 1, 1, 0}, {1024, 8, 1, 1, 0}, {512, 1, 1, 4, 0},
 };
 constexpr int kNumBwdVariants = sizeof(kBwdVariants) / sizeof(kBwdVariants[0]);
 constexpr int kNumBwdDefault = 12;
+// Under the column schedule the (512, 1) rows take 4 rows in flight instead of 2.
+constexpr int kBwdCol512From = 7, kBwdCol512To = 12;
+static_assert(kBwdVariants[kBwdCol512From].tpr == 512 && kBwdVariants[kBwdCol512From].cpt == 1 &&
+                  kBwdVariants[kBwdCol512To].tpr == 512 && kBwdVariants[kBwdCol512To].cpt == 1 &&
+                  kBwdVariants[kBwdCol512To].rg == kBwdVariants[kBwdCol512From].rg,
+              "the column-schedule swap keeps the row layout and block size");
+#ifndef SP_COL_ROW_BLOCKS
+#define SP_COL_ROW_BLOCKS 256  // row + column workgroups the column schedule aims for
+#endif
+constexpr int64_t kColRowBlocks = SP_COL_ROW_BLOCKS;
 
 typedef void (*FwdKernel)(FwdArgs);
 typedef void (*BwdKernel)(BwdArgs);
@@ -920,7 +930,7 @@ typedef void (*BwdKernel)(BwdArgs);
         X(64, 3, 4, 1, 0, __VA_ARGS__), X(64, 4, 4, 1, 0, __VA_ARGS__),                              \
         X(512, 1, 1, 2, 0, __VA_ARGS__), X(512, 2, 1, 2, 0, __VA_ARGS__),                            \
         X(512, 4, 1, 1, 0, __VA_ARGS__), X(1024, 4, 1, 1, 0, __VA_ARGS__),                           \
-        X(1024, 8, 1, 1, 0, __VA_ARGS__)
+        X(1024, 8, 1, 1, 0, __VA_ARGS__), X(512, 1, 1, 4, 0, __VA_ARGS__)
 #define SP_BWD_ENTRY(TPR, CPT, RG, PF, PIPE, DT, NORM, HDR, REGEN, COLS) \
     &sp_bwd_kernel<DT, NORM, TPR, CPT, RG, PF, PIPE != 0, HDR, REGEN, COLS>
 
@@ -1058,18 +1068,29 @@ BwdPlan plan_bwd(const sp_desc_t* d) {
     p.nacc = d->norm == SP_LAYERNORM ? 2 : 1;
     p.variant = pick_bwd_variant(nchunk, SP_BWD_VARIANT);
     if (p.variant < 0) return p;  // unreachable for a validated descriptor
-    const BwdVariant v = kBwdVariants[p.variant];
-    const int step = v.rg * v.pf;  // rows a workgroup takes per step
-    int64_t rpb = (R + SP_BWD_TARGET_BLOCKS - 1) / SP_BWD_TARGET_BLOCKS;
-    rpb = ((rpb + step - 1) / step) * step;
-    if (rpb < step) rpb = step;
-    p.block = v.rg * v.tpr;
-    p.rows_per_block = rpb;
-    p.blocks = R > 0 ? (R + rpb - 1) / rpb : 0;
+    auto tile_rows = [&](int64_t target_blocks) {
+        const BwdVariant v = kBwdVariants[p.variant];
+        const int step = v.rg * v.pf;  // rows a workgroup takes per step
+        int64_t rpb = (R + target_blocks - 1) / target_blocks;
+        rpb = ((rpb + step - 1) / step) * step;
+        if (rpb < step) rpb = step;
+        p.block = v.rg * v.tpr;
+        p.rows_per_block = rpb;
+        p.blocks = R > 0 ? (R + rpb - 1) / rpb : 0;
+    };
+    tile_rows(SP_BWD_TARGET_BLOCKS);
     if (use_columns(R, H, elem_bytes(d->dtype), p.blocks, p.nacc, p.block)) {
+        // The column kernels hold one workgroup per CU: size the row tiles so
+        // that row and column workgroups together fit in one dispatch wave, with
+        // all of a row workgroup's rows in flight where a variant allows it.
         p.col_blocks = (nchunk + kSeg - 1) / kSeg;
+        if (2 * p.col_blocks <= kColRowBlocks) {
+            if (SP_BWD_VARIANT < 0 && p.variant == kBwdCol512From) p.variant = kBwdCol512To;
+            tile_rows(kColRowBlocks - p.col_blocks);
+        }
         return p;
     }
+    const BwdVariant v = kBwdVariants[p.variant];
     p.ws_bytes = (size_t)p.blocks * (size_t)p.nacc * (size_t)H * sizeof(float);
     p.lds_bytes = v.rg > 1 ? (size_t)v.rg * (size_t)p.nacc * (size_t)H * sizeof(float) : 0;
     return p;
