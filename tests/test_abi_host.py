@@ -242,6 +242,8 @@ def test_workspace_size_scales_with_norm(lib):
 @pytest.mark.parametrize("shape,uses_workspace", [
     # (S, B, H, T, dtype, norm): short shards sum dgamma by columns (no workspace)
     ((4096, 1, 4096, 8, "bf16", "ln"), False),   # the LayerNorm T=8 shard, 512 rows
+    ((4080, 1, 4096, 8, "bf16", "ln"), False),   # 510 rows
+    ((4112, 1, 4096, 8, "bf16", "ln"), True),    # 514 rows: past one batch of a column lane
     ((400, 3, 2056, 4, "bf16", "ln"), False),    # 300 rows, a ragged last strip
     ((40, 5, 2000, 2, "f32", "ln"), False),
     ((256, 1, 64, 2, "f32", "rms"), False),
