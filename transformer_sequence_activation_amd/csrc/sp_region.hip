@@ -34,7 +34,7 @@
 #include "sp_region.h"
 
 #ifndef SP_BWD_TARGET_BLOCKS
-#define SP_BWD_TARGET_BLOCKS 256  // workgroups the backward aims for (tiles of rows)
+#define SP_BWD_TARGET_BLOCKS 0  // > 0: workgroups the backward aims for; 0 = the variant's own figure
 #endif
 
 namespace {
@@ -891,15 +891,16 @@ constexpr int block_of(int tpr) { return tpr <= kWave ? kSubWaveBlock : tpr; }
 #endif
 
 // Backward launch variants: (lanes per row, chunks per lane, row groups per
-// workgroup, rows in flight per row group, prefetch of the next step), the
-// default choices in increasing capacity.
+// workgroup, rows in flight per row group, prefetch of the next step, workgroups
+// aimed for), the default choices in increasing capacity.
 struct BwdVariant {
-    int tpr, cpt, rg, pf, pipe;
+    int tpr, cpt, rg, pf, pipe, blocks;
 };
 constexpr BwdVariant kBwdVariants[] = {
-    {16, 1, 16, 1, 0}, {32, 1, 8, 1, 0}, {64, 1, 4, 1, 0},  {32, 3, 8, 1, 0},  {64, 2, 4, 1, 0},
-    {64, 3, 4, 1, 0},  {64, 4, 4, 1, 0}, {512, 1, 1, 2, 0}, {512, 2, 1, 2, 0}, {512, 4, 1, 1, 0},
-    {1024, 4, 1, 1, 0}, {1024, 8, 1, 1, 0}, {512, 1, 1, 4, 0},
+    {16, 1, 16, 1, 0, 256},  {32, 1, 8, 1, 0, 256},   {64, 1, 4, 1, 0, 256},   {32, 3, 8, 1, 0, 256},
+    {64, 2, 4, 1, 0, 256},   {64, 3, 4, 1, 0, 256},   {64, 4, 4, 1, 0, 256},   {512, 1, 1, 2, 0, 256},
+    {512, 2, 1, 1, 0, 512},  {512, 4, 1, 1, 0, 256},  {1024, 4, 1, 1, 0, 256}, {1024, 8, 1, 1, 0, 256},
+    {512, 1, 1, 4, 0, 256},
 };
 constexpr int kNumBwdVariants = sizeof(kBwdVariants) / sizeof(kBwdVariants[0]);
 constexpr int kNumBwdDefault = 12;
@@ -928,7 +929,7 @@ typedef void (*BwdKernel)(BwdArgs);
     X(16, 1, 16, 1, 0, __VA_ARGS__), X(32, 1, 8, 1, 0, __VA_ARGS__), X(64, 1, 4, 1, 0, __VA_ARGS__), \
         X(32, 3, 8, 1, 0, __VA_ARGS__), X(64, 2, 4, 1, 0, __VA_ARGS__),                              \
         X(64, 3, 4, 1, 0, __VA_ARGS__), X(64, 4, 4, 1, 0, __VA_ARGS__),                              \
-        X(512, 1, 1, 2, 0, __VA_ARGS__), X(512, 2, 1, 2, 0, __VA_ARGS__),                            \
+        X(512, 1, 1, 2, 0, __VA_ARGS__), X(512, 2, 1, 1, 0, __VA_ARGS__),                            \
         X(512, 4, 1, 1, 0, __VA_ARGS__), X(1024, 4, 1, 1, 0, __VA_ARGS__),                           \
         X(1024, 8, 1, 1, 0, __VA_ARGS__), X(512, 1, 1, 4, 0, __VA_ARGS__)
 #define SP_BWD_ENTRY(TPR, CPT, RG, PF, PIPE, DT, NORM, HDR, REGEN, COLS) \
@@ -1078,7 +1079,7 @@ BwdPlan plan_bwd(const sp_desc_t* d) {
         p.rows_per_block = rpb;
         p.blocks = R > 0 ? (R + rpb - 1) / rpb : 0;
     };
-    tile_rows(SP_BWD_TARGET_BLOCKS);
+    tile_rows(SP_BWD_TARGET_BLOCKS > 0 ? SP_BWD_TARGET_BLOCKS : kBwdVariants[p.variant].blocks);
     if (use_columns(R, H, elem_bytes(d->dtype), p.blocks, p.nacc, p.block)) {
         // The column kernels hold one workgroup per CU: size the row tiles so
         // that row and column workgroups together fit in one dispatch wave, with
