@@ -297,6 +297,9 @@ EDGE = [
     (4, 400, 3, 2056, "bf16", "ln", 0.1, 1),    # 257 chunks: one ragged chunk past 256
     (2, 200, 1, 8192, "bf16", "ln", 0.2, 1),    # 1024-chunk rows, 100 rows
     (8, 64, 1, 4096, "bf16", "ln", 0.1, 5),     # 8 rows
+    (4, 16, 2, 20480, "bf16", "ln", 0.1, 1),    # 2560-chunk rows: 1024 lanes x 4 chunks, in batches
+    (3, 6, 1, 20480, "bf16", "rms", 0.2, 2),    # the same with a run-time T
+    (2, 8, 1, 10240, "f32", "rms", 0.1, 0),     # fp32, 2560-chunk rows
     (8, 4080, 1, 4096, "bf16", "ln", 0.1, 2),   # 510 rows: column dgamma, ragged last 4-row tile
     (8, 4112, 1, 4096, "bf16", "ln", 0.1, 6),   # 514 rows: just past the column limit, partial rows
 ]

@@ -343,6 +343,119 @@ __global__ __launch_bounds__(BLOCK) void sp_fwd_kernel(const FwdArgs a) {
         col[k] = (ok[k] ? c : a.nchunk - 1) * E;
     }
 
+    if constexpr (BLOCK > 512 && CPT > 2) {
+        // Rows too long for every partial chunk to sit in registers at once: the
+        // chunks go through in batches of KB and h stays packed (16 bytes per
+        // chunk) for the statistics and y.  Same arithmetic, same order.
+        constexpr int KB = (TT > 0 && TT < 4) ? 2 : 1;
+        u32x4 hp[CPT];
+        float s1 = 0.0f;  // LayerNorm: sum of h; RMSNorm: sum of h^2
+#pragma unroll
+        for (int k0 = 0; k0 < CPT; k0 += KB) {
+            float acc[KB][E], res[KB][E];
+            if constexpr (TT > 0) {
+                u32x4 pv[KB][TT], rv[KB];
+#pragma unroll
+                for (int kk = 0; kk < KB; ++kk) {
+                    if (k0 + kk >= CPT) continue;
+                    const int64_t off = (row_elem + col[k0 + kk]) * EB;
+#pragma unroll
+                    for (int t = 0; t < TT; ++t) pv[kk][t] = ld16(a.P[t], off);
+                    rv[kk] = ld16(a.residual, off);
+                }
+#pragma unroll
+                for (int kk = 0; kk < KB; ++kk) {
+                    if (k0 + kk >= CPT) continue;
+                    A::unpack(pv[kk][0], acc[kk]);
+#pragma unroll
+                    for (int t = 1; t < TT; ++t) {
+                        float f[E];
+                        A::unpack(pv[kk][t], f);
+#pragma unroll
+                        for (int e = 0; e < E; ++e) acc[kk][e] = acc[kk][e] + f[e];
+                    }
+                    A::unpack(rv[kk], res[kk]);
+                }
+            } else {
+#pragma unroll
+                for (int kk = 0; kk < KB; ++kk) {
+                    if (k0 + kk >= CPT) continue;
+                    const int64_t off = (row_elem + col[k0 + kk]) * EB;
+                    const u32x4 rv = ld16(a.residual, off);
+                    A::unpack(ld16(a.P[0], off), acc[kk]);
+                    for (int t = 1; t < a.T; ++t) {
+                        float f[E];
+                        A::unpack(ld16(a.P[t], off), f);
+#pragma unroll
+                        for (int e = 0; e < E; ++e) acc[kk][e] = acc[kk][e] + f[e];
+                    }
+                    A::unpack(rv, res[kk]);
+                }
+            }
+#pragma unroll
+            for (int kk = 0; kk < KB; ++kk) {
+                const int k = k0 + kk;
+                if (k >= CPT) continue;
+                const int64_t idx = row_elem + col[k];
+                bool keep[E];
+                keep_flags<E>(a.base + (uint64_t)idx, a.thr, a.key0, a.key1, keep);
+                float hf[E], hv[E];
+                residual_add<E>(acc[kk], res[kk], keep, a.scale, hf);
+                hp[k] = A::pack(hf);
+                A::unpack(hp[k], hv);
+                if (row_ok && ok[k]) {
+                    st16(a.h, idx * EB, hp[k]);
+                    if (a.mask) *reinterpret_cast<typename MW::type*>(a.mask + idx) = MW::make(keep);
+                }
+                if (ok[k]) {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) s1 += a.norm == SP_LAYERNORM ? hv[e] : hv[e] * hv[e];
+                }
+            }
+        }
+        float mu = 0.0f, rs;
+        float q[1] = {s1};
+        if (a.norm == SP_LAYERNORM) {
+            group_sum<TPR, BLOCK, 1>(q);
+            mu = q[0] * a.inv_h;
+            q[0] = 0.0f;
+#pragma unroll
+            for (int k = 0; k < CPT; ++k) {
+                if (!ok[k]) continue;
+                float hv[E];
+                A::unpack(hp[k], hv);
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float dlt = hv[e] - mu;
+                    q[0] += dlt * dlt;
+                }
+            }
+        }
+        group_sum<TPR, BLOCK, 1, false>(q);
+        rs = rsqrtf(q[0] * a.inv_h + a.eps);
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) {
+            float hv[E], gm[E], yv[E];
+            A::unpack(hp[k], hv);
+            load_vec_f32<E>(a.gamma, col[k], gm);
+            if (a.norm == SP_LAYERNORM) {
+                float bt[E];
+                load_vec_f32<E>(a.beta, col[k], bt);
+#pragma unroll
+                for (int e = 0; e < E; ++e) yv[e] = gm[e] * ((hv[e] - mu) * rs) + bt[e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e) yv[e] = gm[e] * (hv[e] * rs);
+            }
+            if (row_ok && ok[k]) st16(a.y, (row_elem + col[k]) * EB, A::pack(yv));
+        }
+        if (row_ok && l == 0) {
+            a.rstd[row] = rs;
+            if (a.norm == SP_LAYERNORM) a.mean[row] = mu;
+        }
+        return;
+    }
+
     // ---- loads: every partial chunk and the residual, issued together ----
     float acc[CPT][E];
     float res[CPT][E];
@@ -548,6 +661,9 @@ __device__ __forceinline__ void bwd_load_step(const BwdArgs& a, int64_t row0, in
 #define SP_COL_BATCH 8
 #endif
 constexpr int kColBatch = SP_COL_BATCH;
+// 1024-lane workgroups have half the registers per lane: half the batch (the
+// same rows per batch, as there are twice the row offsets).
+constexpr int col_batch(int block) { return block > 512 ? (kColBatch + 1) / 2 : kColBatch; }
 #ifndef SP_COL_SEG
 #define SP_COL_SEG 8
 #endif
@@ -560,7 +676,7 @@ __device__ __forceinline__ void bwd_columns(const BwdArgs& a, int strip) {
     constexpr int EB = A::kBytes;
     constexpr int NACC = LN ? 2 : 1;
     constexpr int kRO = BLOCK / kSeg;  // row offsets
-    constexpr int kB = kColBatch;      // steps whose loads are in flight together
+    constexpr int kB = col_batch(BLOCK);  // steps whose loads are in flight together
     constexpr int NW = BLOCK / kWave;
     __shared__ float cred[NW][NACC][kSeg * E];
 
@@ -676,9 +792,14 @@ __global__ __launch_bounds__(RG* TPR) void sp_bwd_kernel(const BwdArgs a) {
         ok[k] = c < a.nchunk;
         col[k] = (ok[k] ? c : a.nchunk - 1) * E;
     }
+    // gamma: held in registers, or (long rows, 1024-lane workgroups) read again
+    // where it is used -- a small array that stays in the caches
+    constexpr bool kGammaRegs = !(BLOCK > 512 && CPT > 2);
     float gam[CPT][E];
+    if constexpr (kGammaRegs) {
 #pragma unroll
-    for (int k = 0; k < CPT; ++k) load_vec_f32<E>(a.gamma, col[k], gam[k]);
+        for (int k = 0; k < CPT; ++k) load_vec_f32<E>(a.gamma, col[k], gam[k]);
+    }
 
     float dg[CPT][E], db[CPT][LN ? E : 1];
 #pragma unroll
@@ -711,14 +832,15 @@ __global__ __launch_bounds__(RG* TPR) void sp_bwd_kernel(const BwdArgs a) {
             s[2 * p + 1] = 0.0f;
 #pragma unroll
             for (int k = 0; k < CPT; ++k) {
-                float dyv[E], hv[E];
+                float dyv[E], hv[E], gk[E];
                 A::unpack(rows[p].dy[k], dyv);
                 A::unpack(rows[p].hh[k], hv);
+                if constexpr (!kGammaRegs) load_vec_f32<E>(a.gamma, col[k], gk);
                 if (ok[k]) {
 #pragma unroll
                     for (int e = 0; e < E; ++e) {
                         const float x = (hv[e] - rows[p].mu) * rows[p].rs;
-                        const float g = dyv[e] * gam[k][e];
+                        const float g = dyv[e] * (kGammaRegs ? gam[k][e] : gk[e]);
                         if constexpr (LN) s[2 * p] += g;
                         s[2 * p + 1] += g * x;
                         if (row_ok && partial_rows) {
@@ -740,10 +862,11 @@ __global__ __launch_bounds__(RG* TPR) void sp_bwd_kernel(const BwdArgs a) {
             const int64_t row_elem = (row_ok ? row : 0) * (int64_t)a.H;
 #pragma unroll
             for (int k = 0; k < CPT; ++k) {
-                float dyv[E], hv[E], drv[E], dh[E], dp[E];
+                float dyv[E], hv[E], drv[E], dh[E], dp[E], gk[E];
                 bool keep[E];
                 A::unpack(rows[p].dy[k], dyv);
                 A::unpack(rows[p].hh[k], hv);
+                if constexpr (!kGammaRegs) load_vec_f32<E>(a.gamma, col[k], gk);
                 if constexpr (HAS_DR) A::unpack(rows[p].dr[k], drv);
                 if constexpr (REGEN)
                     keep_flags<E>(a.base + (uint64_t)(row_elem + col[k]), a.thr, a.key0, a.key1, keep);
@@ -752,7 +875,7 @@ __global__ __launch_bounds__(RG* TPR) void sp_bwd_kernel(const BwdArgs a) {
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
                     const float x = (hv[e] - rows[p].mu) * rows[p].rs;
-                    const float g = dyv[e] * gam[k][e];
+                    const float g = dyv[e] * (kGammaRegs ? gam[k][e] : gk[e]);
                     float v = rows[p].rs * (g - c1 - x * c2);
                     if constexpr (HAS_DR) v += drv[e];
                     dh[e] = v;
@@ -1058,7 +1181,7 @@ constexpr int64_t kFinishLaunchBytes = (int64_t)16 << 20;
 bool use_columns(int64_t R, int64_t H, int eb, int64_t G, int nacc, int block) {
     if (SP_BWD_DG == 1 || R == 0) return false;
     if (SP_BWD_DG == 2) return true;
-    if (R > (int64_t)(block / kSeg) * kColBatch) return false;
+    if (R > (int64_t)(block / kSeg) * col_batch(block)) return false;
     return 2 * R * H * eb <= 2 * G * nacc * H * 4 + kFinishLaunchBytes;
 }
 
