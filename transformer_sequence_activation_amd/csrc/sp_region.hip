@@ -99,6 +99,9 @@ struct Act<SP_F32> {
 #ifndef SP_NT_STORES
 #define SP_NT_STORES 1
 #endif
+#ifndef SP_EARLY_FLAGS
+#define SP_EARLY_FLAGS 1  // forward with T <= 2: keep flags made while the loads are in flight
+#endif
 __device__ __forceinline__ u32x4 ld16(const void* base, int64_t byte_off) {
     const u32x4* p = reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(base) + byte_off);
 #if SP_NT_LOADS
@@ -459,6 +462,10 @@ __global__ __launch_bounds__(BLOCK) void sp_fwd_kernel(const FwdArgs a) {
     // ---- loads: every partial chunk and the residual, issued together ----
     float acc[CPT][E];
     float res[CPT][E];
+    // With few partials the generator is a visible share of the work: its flags
+    // (one bit per element) are then made while the loads are in flight.
+    constexpr bool kEarlyFlags = SP_EARLY_FLAGS && TT > 0 && TT <= 2;
+    uint32_t kbits[CPT];
     if constexpr (TT > 0) {
         u32x4 pv[CPT][TT];
         u32x4 rv[CPT];
@@ -468,6 +475,16 @@ __global__ __launch_bounds__(BLOCK) void sp_fwd_kernel(const FwdArgs a) {
 #pragma unroll
             for (int t = 0; t < TT; ++t) pv[k][t] = ld16(a.P[t], off);
             rv[k] = ld16(a.residual, off);
+        }
+        if constexpr (kEarlyFlags) {
+#pragma unroll
+            for (int k = 0; k < CPT; ++k) {
+                bool kf[E];
+                keep_flags<E>(a.base + (uint64_t)(row_elem + col[k]), a.thr, a.key0, a.key1, kf);
+                kbits[k] = 0;
+#pragma unroll
+                for (int e = 0; e < E; ++e) kbits[k] |= (uint32_t)kf[e] << e;
+            }
         }
 #pragma unroll
         for (int k = 0; k < CPT; ++k) {
@@ -516,7 +533,12 @@ __global__ __launch_bounds__(BLOCK) void sp_fwd_kernel(const FwdArgs a) {
     for (int k = 0; k < CPT; ++k) {
         const int64_t idx = row_elem + col[k];
         bool keep[E];
-        keep_flags<E>(a.base + (uint64_t)idx, a.thr, a.key0, a.key1, keep);
+        if constexpr (kEarlyFlags) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) keep[e] = (kbits[k] >> e) & 1u;
+        } else {
+            keep_flags<E>(a.base + (uint64_t)idx, a.thr, a.key0, a.key1, keep);
+        }
         float hf[E];
         residual_add<E>(acc[k], res[k], keep, a.scale, hf);
         const u32x4 hp = A::pack(hf);
