@@ -1,5 +1,6 @@
-"""Summarise a rocprofv3 results database: per-kernel durations and, when the
-run collected them, the FETCH_SIZE / WRITE_SIZE hardware counters.
+"""Summarise a rocprofv3 results database: per-kernel durations (from the
+kernel trace, and rocprofv3's own --stats summary) and, when the run collected
+them, the FETCH_SIZE / WRITE_SIZE hardware counters.
 
     python -m transformer_sequence_activation_amd.rocprof_summary RESULTS.db [...]
         [--copy-bytes N] [--filter SUBSTRING]
@@ -39,6 +40,17 @@ def kernel_stats(con, filt=None):
     return sorted(out, key=lambda r: -r[1] * r[2])
 
 
+def rocprof_stats(con, filt=None):
+    """rocprofv3's own --stats summary, kept in the results database as the
+    top_kernels view: (name, calls, total_us, average_us, percent)."""
+    tables = {r[0] for r in con.execute("select name from sqlite_master where type in ('table','view')")}
+    if "top_kernels" not in tables:
+        return []
+    rows = con.execute("select name, total_calls, total_duration, average, percentage from top_kernels")
+    return [(short_name(n), int(c), float(t), float(av), float(pc)) for n, c, t, av, pc in rows
+            if not filt or filt in n]
+
+
 def counters(con):
     """{kernel short name: {counter: [values per dispatch]}} if counters were collected."""
     tables = {r[0] for r in con.execute("select name from sqlite_master where type in ('table','view')")}
@@ -68,6 +80,12 @@ def main():
         print(f"{'kernel':90s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'med_us':>9s} {'max_us':>9s}")
         for k, n, avg, mn, med, mx in kernel_stats(con, a.filter):
             print(f"{k:90s} {n:6d} {avg:9.3f} {mn:9.3f} {med:9.3f} {mx:9.3f}")
+        st = rocprof_stats(con, a.filter)
+        if st:
+            print("\nrocprofv3 --stats (top_kernels view)")
+            print(f"{'kernel':90s} {'calls':>6s} {'total_us':>11s} {'avg_us':>9s} {'percent':>8s}")
+            for k, n, tot, avg, pc in st:
+                print(f"{k:90s} {n:6d} {tot:11.1f} {avg:9.3f} {pc:8.2f}")
         cnt = counters(con)
         if cnt:
             scale = {}
