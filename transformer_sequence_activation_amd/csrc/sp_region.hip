@@ -18,11 +18,13 @@
 //     element index): one generator call gives the four words of four
 //     consecutive elements, so a bf16 chunk costs two calls and no state is
 //     kept between launches.
-//   * The backward accumulates dgamma/dbeta for its columns in registers over a
-//     tile of rows, combines the row groups of a workgroup in LDS, writes one
-//     fp32 partial row per workgroup, and a second small kernel sums those
-//     partials in a fixed order: no float atomics, results are run-to-run
-//     identical.
+//   * dgamma/dbeta have two schedules, chosen per shape by the host.  Short
+//     shards: the first workgroups of the backward launch each sum a 128-byte
+//     column strip over all rows (dY and h read a second time, no workspace).
+//     Long shards: the row workgroups accumulate their columns in registers,
+//     write one fp32 partial row each, and a second small kernel sums those
+//     rows.  Both add in a fixed order: no float atomics, results are
+//     run-to-run identical.
 //   * No MFMA: nothing here is a contraction; the path is bound by HBM.
 #include <hip/hip_runtime.h>
 
@@ -777,9 +779,11 @@ __device__ __forceinline__ void bwd_columns(const BwdArgs& a, int strip) {
 // rows_per_block rows.  In each step every row group takes PF rows whose loads
 // are all in flight together, reduces the PF rows' two sums in one pass, then
 // writes their gradients.  With PIPE the next step's loads are issued before
-// this step is computed.  dgamma (and dbeta) accumulate in registers and each
-// workgroup writes one partial row.  With REGEN the keep flags are generated
-// again from (seed, global index) instead of read from a mask tensor.
+// this step is computed.  Without COLS, dgamma (and dbeta) accumulate in
+// registers and each workgroup writes one partial row; with COLS the first
+// col_blocks workgroups are column workgroups (bwd_columns) and the row
+// workgroups leave dgamma alone.  With REGEN the keep flags are generated again
+// from (seed, global index) instead of read from a mask tensor.
 template <int DT, int NORM, int TPR, int CPT, int RG, int PF, bool PIPE, bool HAS_DR, bool REGEN, bool COLS>
 __global__ __launch_bounds__(RG* TPR) void sp_bwd_kernel(const BwdArgs a) {
     using A = Act<DT>;
