@@ -363,6 +363,28 @@ def test_rounding_ties_to_even():
     assert np.all((exact & 0xFFFF) == 0x8000)
 
 
+def test_nonfinite_input_stays_in_its_row():
+    """An infinite partial element (kept by dropout) makes only its own token row
+    non-finite; every other row of the shard still matches the oracle."""
+    print("\n[case] +inf in one partial element", flush=True)
+    c = _edge_case(2, 64, 1, 256, "bf16", "rms", 0.1, 1)
+    w, j = c.w, 1
+    o = oracle_fwd(c, j)
+    r_bad = 5
+    k_bad = int(np.flatnonzero(o["mask"][r_bad])[0])  # an element the mask keeps
+    P0 = c.P[0].clone()
+    W.shard(P0, w, j)[r_bad, k_bad] = float("inf")
+    c.P = [P0] + c.P[1:]
+    g = gpu_fwd(c, j)
+    torch.cuda.synchronize()
+    o = oracle_fwd(c, j)
+    rows = [r for r in range(w.R) if r != r_bad]
+    compare_fwd(w, g, {k: (None if v is None else v[rows]) for k, v in o.items()}, rows=rows)
+    h_bad = as_f64(to_np(g["h"])[r_bad], "bf16")
+    assert np.isinf(h_bad[k_bad]) and np.isfinite(np.delete(h_bad, k_bad)).all()
+    assert not np.isfinite(as_f64(to_np(g["y"])[r_bad], "bf16")).all()
+
+
 def test_empty_shard():
     print("\n[case] empty shard", flush=True)
     d = sp.make_desc(0, 2, 256, 2, 1, "bf16", "ln", 1e-5, 0.1, 1)
