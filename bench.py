@@ -17,7 +17,8 @@ buffer sets between HIP event pairs recorded on the kernels' stream: elapsed
 time / launches gives the per-launch durations behind "roofline" (the forward is
 the dominant kernel).  A 1 GiB device copy on the same stream is timed as an
 achievable-bandwidth reference.  The other workloads are measured the same way
-with fewer steps and reported under "workloads".
+with fewer steps and reported under "workloads"; a step of those covers every
+shard the workload lists (MiniMind: shards 0 and 1; long sequence: all 8).
 
 cpu_baseline: the CPU oracle on a bounded sample of the headline shard, with a
 parity check of that sample against the GPU's outputs: once on one thread
@@ -509,7 +510,7 @@ def main():
     if not args.no_secondary:
         for name, flags in SECONDARY:
             ws = W.WORKLOADS[name]
-            shards = ws.shards if len(ws.shards) > 2 else (ws.shards[0],)
+            shards = tuple(ws.shards)  # every shard the workload lists, one after another
             K2 = 40 if len(shards) > 2 else 400
             r, s2, st2 = measure(sp, ws, tuple(shards), K2, max(10, K2 // 10), stream, flags)
             label = name + ("+recompute_mask" if flags & sp.SP_FLAG_RECOMPUTE_MASK else "")
