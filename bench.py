@@ -435,7 +435,7 @@ def profile_pass(sp, w, stream):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: this build runs one "
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the library runs one "
               "rank's shard on one GPU and has no collectives.", file=sys.stderr)
         sys.exit(2)
 
