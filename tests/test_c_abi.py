@@ -1,0 +1,48 @@
+"""The C ABI from C: tests/c_abi_check.c, a C99 program that includes only
+include/sp_region.h and the HIP runtime API, compared with the C oracle.
+
+CPU: it compiles as strict C99 with every warning an error (the header is
+valid C) and links against libsp_region.so and the oracle.
+GPU: it runs, on a short LayerNorm shard (column dgamma) and a long RMSNorm
+shard (partial rows), and matches the oracle.
+"""
+import os
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+PKG = os.path.join(ROOT, "transformer_sequence_activation_amd")
+ORACLE = os.path.join(ROOT, "oracle")
+
+
+def build_check(tmp_path):
+    import oracle
+    import transformer_sequence_activation_amd as sp
+
+    sp.load()        # the library must be built
+    oracle.lib()     # builds oracle/libsp_oracle.so if needed
+    out = str(tmp_path / "c_abi_check")
+    cmd = ["gcc", "-std=c99", "-O1", "-Wall", "-Wextra", "-Werror", "-pedantic",
+           "-D__HIP_PLATFORM_AMD__", "-isystem", f"{ROCM}/include", f"-I{ROOT}/include",
+           os.path.join(ROOT, "tests", "c_abi_check.c"), "-o", out,
+           f"-L{PKG}", "-lsp_region", f"-L{ORACLE}", "-lsp_oracle", f"-L{ROCM}/lib", "-lamdhip64", "-lm",
+           f"-Wl,-rpath,{PKG}", f"-Wl,-rpath,{ORACLE}", f"-Wl,-rpath,{ROCM}/lib"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    return out
+
+
+def test_c_program_compiles_against_the_header(tmp_path):
+    build_check(tmp_path)
+
+
+@pytest.mark.gpu
+def test_c_program_matches_the_oracle(tmp_path):
+    exe = build_check(tmp_path)
+    print("\n[case] tests/c_abi_check.c on the GPU", flush=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    print(r.stdout, r.stderr)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "matches the oracle" in r.stdout
