@@ -261,6 +261,57 @@ def test_long_sequence_all_shards():
     assert abs(keep_total - Nt * (1 - w.p)) <= 5 * math.sqrt(Nt * w.p * (1 - w.p))
 
 
+def test_concurrent_calls_from_threads_and_streams():
+    """The library holds no state: two host threads, each with its own stream,
+    workspace and shard, enqueue forward + backward at the same time; every
+    output equals the sequential run bit for bit."""
+    import threading
+    w = W.WORKLOADS["minimind_T2_S2048_B2_H768"]
+    print(f"\n[case] {w.name}: shards 0 and 1 from two threads on two streams", flush=True)
+    c = Case(w, "cuda")
+    ref = {}
+    for j in (0, 1):
+        f = gpu_fwd(c, j)
+        b = gpu_bwd(c, j, f)
+        ref[j] = (f, b)
+    torch.cuda.synchronize()
+    got, errors = {}, []
+    streams = {j: torch.cuda.Stream() for j in (0, 1)}
+    barrier = threading.Barrier(2)
+
+    def run(j):
+        try:
+            torch.cuda.set_device(0)
+            s = streams[j]
+            with torch.cuda.stream(s):
+                barrier.wait()
+                outs = []
+                for _ in range(20):
+                    f = sp.forward(gdesc(w, j), c.P, c.shard(c.res, j), c.gamma, c.beta, stream=s)
+                    b = sp.backward(gdesc(w, j), c.shard(c.dY, j), f["h"], f["mask"], f["mean"], f["rstd"],
+                                    c.gamma, stream=s)
+                    outs.append((f, b))
+                s.synchronize()
+                got[j] = outs
+        except Exception as e:  # reported by the main thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=run, args=(j,)) for j in (0, 1)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for j in (0, 1):
+        f0, b0 = ref[j]
+        for f, b in got[j]:
+            for k in ("h", "y", "mask", "rstd"):
+                assert torch.equal(f0[k], f[k]), (j, k)
+            for k in ("d_res", "dP", "dgamma"):
+                assert torch.equal(b0[k], b[k]), (j, k)
+
+
 def test_runs_are_bitwise_identical():
     w = W.WORKLOADS["layernorm_T8_S4096_B1_H4096"]
     print(f"\n[case] {w.name}: two runs bitwise", flush=True)
