@@ -176,6 +176,35 @@ def test_allreduce_equals_reduce_scatter_plus_all_gather(T):
     assert np.array_equal(ring, exact)
 
 
+@pytest.mark.parametrize("T,norm", [(2, oracle.RMSNORM), (4, oracle.LAYERNORM), (8, oracle.RMSNORM)])
+def test_shards_concatenate_to_the_unsharded_run(T, norm):
+    """Real-valued fp32 data with dropout: the T shards' h, y and mask,
+    concatenated, are bit-identical to one unsharded run (T = 1) fed the fp32
+    sum of the partials taken in the same order -- concat_j sum_t P_t^(j) equals
+    sum_t P_t, and the rest of the region is per element and per token row."""
+    S, B, H = 8 * T, 2, 24
+    rng = np.random.default_rng(40 + T)
+    P = [(rng.standard_normal((S, B, H)) / math.sqrt(T)).astype(np.float32) for _ in range(T)]
+    res = rng.standard_normal((S, B, H)).astype(np.float32)
+    gam = 1 + 0.02 * rng.standard_normal(H)
+    bet = 0.02 * rng.standard_normal(H) if norm == oracle.LAYERNORM else None
+    eps = 1e-5 if norm == oracle.LAYERNORM else 1e-6
+    total = P[0].copy()
+    for t in range(1, T):
+        total = total + P[t]  # fp32 adds in t order
+    one = oracle.fwd(desc(S, B, H, 1, 0, oracle.F32, norm, eps, 0.25), [total.reshape(-1, H)],
+                     res.reshape(-1, H), gam, bet)
+    parts = {k: [] for k in ("h", "y", "mask")}
+    for j in range(T):
+        d = desc(S, B, H, T, j, oracle.F32, norm, eps, 0.25)
+        out = oracle.fwd(d, [shard_rows(P[t], S, B, H, T, j) for t in range(T)],
+                         shard_rows(res, S, B, H, T, j), gam, bet)
+        for k in parts:
+            parts[k].append(out[k])
+    for k in parts:
+        assert np.array_equal(np.concatenate(parts[k]), one[k]), k
+
+
 def test_mask_is_keyed_on_the_global_index():
     """Shard masks for any T tile the mask of the whole tensor (the mask must
     correspond along the sequence whatever the split)."""
