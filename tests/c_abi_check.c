@@ -9,6 +9,7 @@
  * finish kernel, with a workspace).  Bar: mask and h byte-identical; y,
  * d_residual, dP, dgamma, dbeta within 1e-2 relative (plus 1e-2 of the rms of
  * the reference); rstd and mean within 1e-5.  Exit status 0 = pass.
+ * --any-schedule: do not check which dgamma schedule each shard gets.
  */
 #include <hip/hip_runtime_api.h>
 #include <math.h>
@@ -75,6 +76,7 @@ static double bf16_val(uint16_t b)
 }
 
 static int failures = 0;
+static int any_schedule = 0; /* --any-schedule: a build that forces one dgamma schedule */
 
 static void close_to(const char* what, const double* got, const double* ref, int64_t n, double rtol)
 {
@@ -174,7 +176,7 @@ static void check_shard(int64_t S, int64_t B, int64_t H, int32_t T, int32_t j, i
         return;
     }
     ws = sp_region_bwd_workspace_size(&d);
-    if ((ws > 0) != expect_ws) {
+    if (!any_schedule && (ws > 0) != expect_ws) {
         fprintf(stderr, "  workspace of %zu bytes, expected %s\n", ws, expect_ws ? "some" : "none");
         ++failures;
     }
@@ -286,10 +288,11 @@ static void check_shard(int64_t S, int64_t B, int64_t H, int32_t T, int32_t j, i
     free(dres_o); free(dP_o); free(dgam_o); free(dbet_o); free(a); free(b);
 }
 
-int main(void)
+int main(int argc, char** argv)
 {
     sp_desc_t bad;
     g_state = 1234;
+    any_schedule = argc > 1 && strcmp(argv[1], "--any-schedule") == 0;
     if (sp_region_version() <= 0) {
         fprintf(stderr, "bad version\n");
         return 1;

@@ -40,9 +40,15 @@ def test_c_program_compiles_against_the_header(tmp_path):
 
 @pytest.mark.gpu
 def test_c_program_matches_the_oracle(tmp_path):
+    import transformer_sequence_activation_amd as sp
+
     exe = build_check(tmp_path)
+    # a tuning build may force one dgamma schedule for every shape; the default
+    # build gives the long shard a workspace (partial rows)
+    forced = sp.sp_region_bwd_workspace_size(sp.make_desc(2048, 1, 256, 4, 2, "bf16", "rms")) == 0
     print("\n[case] tests/c_abi_check.c on the GPU", flush=True)
-    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    r = subprocess.run([exe] + (["--any-schedule"] if forced else []), capture_output=True, text=True,
+                       timeout=120)
     print(r.stdout, r.stderr)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "matches the oracle" in r.stdout
