@@ -251,6 +251,9 @@ def test_workspace_size_scales_with_norm(lib):
     ((2048, 2, 768, 2, "bf16", "rms"), True),    # 2048 rows of 768
     ((32768, 1, 8192, 8, "bf16", "rms"), True),
     ((4096, 4, 128, 4, "bf16", "ln"), True),     # 4096 short rows
+    ((16, 2, 20480, 4, "bf16", "ln"), False),    # 8 long rows (1024-lane workgroups)
+    ((1040, 1, 20480, 2, "bf16", "rms"), True),  # 520 long rows: past the 512-row column limit
+    ((1040, 1, 65536, 2, "bf16", "ln"), True),
 ])
 def test_backward_schedule_by_shape(lib, shape, uses_workspace):
     """Both dgamma schedules are exercised by the GPU parity shapes listed here."""
