@@ -4,8 +4,8 @@
 // with no arithmetic:
 //   copy    : one 16-byte nontemporal load and store per lane, grid-stride loop,
 //             at several sizes and grid sizes (the achievable-bandwidth ceiling);
-//   fwd_pat : the forward's access pattern: T=8 partial streams + residual read,
-//             two 16-byte streams and one 8-byte stream written;
+//   fwd_pat : the forward's access pattern: T partial streams (T = 8 or 2) +
+//             residual read, two 16-byte streams and one 8-byte stream written;
 //   bwd_pat : the backward's pattern: two 16-byte streams and one 8-byte stream
 //             read, two 16-byte streams written.
 // Prints one JSON object per measurement.  Usage: stream_probe [max_buffer_GiB]
@@ -34,7 +34,8 @@ __global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ a, 
     for (; i < n; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(a + i), b + i);
 }
 
-// n chunks per stream; p holds 8 consecutive streams, r one more
+// n chunks per stream; p holds T consecutive streams, r one more
+template <int T>
 __global__ __launch_bounds__(512) void fwd_pattern_kernel(const u32x4* __restrict__ p, const u32x4* __restrict__ r,
                                                           u32x4* __restrict__ h, u32x4* __restrict__ y,
                                                           u32x2* __restrict__ m, int64_t n) {
@@ -42,7 +43,7 @@ __global__ __launch_bounds__(512) void fwd_pattern_kernel(const u32x4* __restric
     if (i >= n) return;
     u32x4 acc = __builtin_nontemporal_load(r + i);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) acc ^= __builtin_nontemporal_load(p + t * n + i);
+    for (int t = 0; t < T; ++t) acc ^= __builtin_nontemporal_load(p + t * n + i);
     __builtin_nontemporal_store(acc, h + i);
     __builtin_nontemporal_store(acc + 1u, y + i);
     const u32x2 mm = {acc.x, acc.y};
@@ -110,28 +111,38 @@ int main(int argc, char** argv) {
                    (long long)bytes, g, us, 2.0 * bytes / us / 1e3);
         }
     }
-    // stream sizes of the LayerNorm T=8 H=4096 shard (4 MiB bf16 per stream) and the
-    // large-hidden T=8 H=8192 B=2 shard (32 MiB)
-    for (int64_t sb : {(int64_t)4 << 20, (int64_t)32 << 20}) {
+    // stream sizes of the MiniMind T=2 shard (3 MiB bf16 per stream), the LayerNorm
+    // T=8 H=4096 shard (4 MiB) and the large-hidden T=8 H=8192 B=2 shard (32 MiB)
+    struct Case {
+        int T;
+        int64_t sb;
+    };
+    const Case cases[] = {{2, (int64_t)3 << 20}, {8, (int64_t)4 << 20}, {8, (int64_t)32 << 20}};
+    for (const Case& c : cases) {
+        const int64_t sb = c.sb;
         const int64_t n = sb / 16;
         const int g = (int)((n + 511) / 512);
         {
-            const int64_t rin = 9 * sb, rout = 3 * sb;
+            const int64_t rin = (c.T + 1) * sb, rout = 3 * sb;
             int nrot = (int)(cap / rin);
             if (nrot > 16) nrot = 16;
             const double us = tm.us_per_launch(
                 [&](int k) {
                     char* a = A + (int64_t)(k % nrot) * rin;
                     char* b = B + (int64_t)(k % nrot) * rout;
-                    fwd_pattern_kernel<<<g, 512>>>((const u32x4*)a, (const u32x4*)(a + 8 * sb), (u32x4*)b,
-                                                   (u32x4*)(b + sb), (u32x2*)(b + 2 * sb), n);
+                    if (c.T == 2)
+                        fwd_pattern_kernel<2><<<g, 512>>>((const u32x4*)a, (const u32x4*)(a + 2 * sb), (u32x4*)b,
+                                                          (u32x4*)(b + sb), (u32x2*)(b + 2 * sb), n);
+                    else
+                        fwd_pattern_kernel<8><<<g, 512>>>((const u32x4*)a, (const u32x4*)(a + 8 * sb), (u32x4*)b,
+                                                          (u32x4*)(b + sb), (u32x2*)(b + 2 * sb), n);
                 },
                 reps);
-            const double moved = 9.0 * sb + 2.5 * sb;
-            printf("{\"probe\": \"fwd_pattern\", \"stream_bytes\": %lld, \"us\": %.3f, \"GBs\": %.1f}\n",
-                   (long long)sb, us, moved / us / 1e3);
+            const double moved = (c.T + 1.0) * sb + 2.5 * sb;
+            printf("{\"probe\": \"fwd_pattern\", \"T\": %d, \"stream_bytes\": %lld, \"us\": %.3f, \"GBs\": %.1f}\n",
+                   c.T, (long long)sb, us, moved / us / 1e3);
         }
-        {
+        if (c.T == 8 || sb == ((int64_t)3 << 20)) {
             const int64_t rin = 5 * sb / 2, rout = 2 * sb;
             int nrot = (int)(cap / rin);
             if (nrot > 16) nrot = 16;
