@@ -11,7 +11,9 @@ the 256 MB Infinity Cache, so every step reads HBM.
 
 Timed region: K steps launched by replaying captured HIP graphs (so host launch
 cost does not throttle the GPU), bracketed by synchronize on both sides and
-timed by the host clock.  value = algorithmic bytes of fwd + bwd per step / time
+timed by the host clock.  A graph runs the forwards of all buffer sets, then
+their backwards, so a batch's backward does not find its forward's outputs in
+the caches.  value = algorithmic bytes of fwd + bwd per step / time
 per step.  A second pass replays forward-only and backward-only graphs over all
 buffer sets between HIP event pairs recorded on the kernels' stream: elapsed
 time / launches gives the per-launch durations behind "roofline" (the forward is
@@ -153,8 +155,14 @@ def make_source(w, shards):
     return src
 
 
-def measure(sp, w, shards, K, Wm, stream, flags=0):
-    """Time K steps (graph replay, host clock) and per-launch durations (events)."""
+def measure(sp, w, shards, K, Wm, stream, flags=0, paired=False):
+    """Time K steps (graph replay, host clock) and per-launch durations (events).
+
+    The timed graphs run the forwards of all buffer sets, then their backwards,
+    so other sets' traffic (more than the 256 MB Infinity Cache) separates a
+    batch's forward from its backward, as the rest of a model would: the
+    backward cannot find h and the mask still cached.  paired=True runs each
+    set's forward and backward back to back instead."""
     import torch
 
     src = make_source(w, shards)
@@ -184,8 +192,22 @@ def measure(sp, w, shards, K, Wm, stream, flags=0):
             fn()
         return g
 
-    g_all = capture(lambda: [s.step() for s in sets])
-    g_rem = capture(lambda: [s.step() for s in sets[:rem]]) if rem else None
+    def steps(sel):
+        def run():
+            if paired:
+                for s in sel:
+                    s.step()
+                return
+            for s in sel:
+                for sh in s.shards:
+                    sh.fwd()
+            for s in sel:
+                for sh in s.shards:
+                    sh.bwd()
+        return run
+
+    g_all = capture(steps(sets))
+    g_rem = capture(steps(sets[:rem])) if rem else None
     g_fwd = capture(lambda: [sh.fwd() for s in sets for sh in s.shards])
     g_bwd = capture(lambda: [sh.bwd() for s in sets for sh in s.shards])
     torch.cuda.synchronize()

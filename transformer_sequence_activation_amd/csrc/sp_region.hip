@@ -1230,9 +1230,10 @@ BwdPlan plan_bwd(const sp_desc_t* d) {
     };
     tile_rows(SP_BWD_TARGET_BLOCKS > 0 ? SP_BWD_TARGET_BLOCKS : kBwdVariants[p.variant].blocks);
     if (use_columns(R, H, elem_bytes(d->dtype), p.blocks, p.nacc, p.block)) {
-        // The column kernels hold one workgroup per CU: size the row tiles so
-        // that row and column workgroups together fit in one dispatch wave, with
-        // all of a row workgroup's rows in flight where a variant allows it.
+        // Column kernels are register-heavy (the 512-lane one fits one workgroup
+        // per CU): size the row tiles so that row and column workgroups together
+        // number one per CU, with all of a row workgroup's rows in flight where a
+        // variant allows it.
         p.col_blocks = (nchunk + kSeg - 1) / kSeg;
         if (2 * p.col_blocks <= kColRowBlocks) {
             if (SP_BWD_VARIANT < 0 && p.variant == kBwdCol512From) p.variant = kBwdCol512To;
