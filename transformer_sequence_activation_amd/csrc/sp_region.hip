@@ -778,13 +778,12 @@ __device__ __forceinline__ void bwd_columns(const BwdArgs& a, int strip) {
 // A workgroup holds RG row groups of TPR lanes and walks a tile of
 // rows_per_block rows.  In each step every row group takes PF rows whose loads
 // are all in flight together, reduces the PF rows' two sums in one pass, then
-// writes their gradients.  With PIPE the next step's loads are issued before
-// this step is computed.  Without COLS, dgamma (and dbeta) accumulate in
+// writes their gradients.  Without COLS, dgamma (and dbeta) accumulate in
 // registers and each workgroup writes one partial row; with COLS the first
 // col_blocks workgroups are column workgroups (bwd_columns) and the row
 // workgroups leave dgamma alone.  With REGEN the keep flags are generated again
 // from (seed, global index) instead of read from a mask tensor.
-template <int DT, int NORM, int TPR, int CPT, int RG, int PF, bool PIPE, bool HAS_DR, bool REGEN, bool COLS>
+template <int DT, int NORM, int TPR, int CPT, int RG, int PF, bool HAS_DR, bool REGEN, bool COLS>
 __global__ __launch_bounds__(RG* TPR) void sp_bwd_kernel(const BwdArgs a) {
     using A = Act<DT>;
     constexpr bool LN = NORM == SP_LAYERNORM;
@@ -844,11 +843,6 @@ __global__ __launch_bounds__(RG* TPR) void sp_bwd_kernel(const BwdArgs a) {
     load_step(row_begin + (int64_t)rg * PF, rows);
     for (int it = 0; it < iters; ++it) {
         const int64_t row0 = row_begin + (int64_t)it * STEP + (int64_t)rg * PF;
-        BwdRow<CPT, E> nxt[PIPE ? PF : 1];
-        if constexpr (PIPE) {
-            if (it + 1 < iters)
-                load_step(row0 + STEP, nxt);
-        }
         // pass 1: the two row sums of every row, and the dgamma / dbeta terms
         float s[2 * PF];
 #pragma unroll
@@ -914,14 +908,7 @@ __global__ __launch_bounds__(RG* TPR) void sp_bwd_kernel(const BwdArgs a) {
                 }
             }
         }
-        if (it + 1 < iters) {
-            if constexpr (PIPE) {
-#pragma unroll
-                for (int p = 0; p < PF; ++p) rows[p] = nxt[p];
-            } else {
-                load_step(row0 + STEP, rows);
-            }
-        }
+        if (it + 1 < iters) load_step(row0 + STEP, rows);
     }
 
     // ---- this workgroup's partial dgamma / dbeta row ----
@@ -1017,11 +1004,16 @@ __global__ __launch_bounds__(kFinGroups* kFinSlices) void sp_dgamma_finish_kerne
 struct Layout {
     int tpr, cpt;
 };
-// In increasing capacity (tpr * cpt chunks); the first that holds the row is used.
-constexpr Layout kLayouts[] = {
-    {16, 1},  {32, 1},  {64, 1},  {32, 3},   {64, 2},    {64, 3},
-    {64, 4},  {512, 1}, {512, 2}, {512, 4}, {1024, 4}, {1024, 8},
-};
+// In increasing capacity (tpr * cpt chunks); the first that holds the row is
+// used.  X(lanes per row, chunks per lane, ...): the host table and the kernel
+// tables below are both generated from this list.
+#define SP_LAYOUT_LIST(X, ...)                                                                    \
+    X(16, 1, __VA_ARGS__), X(32, 1, __VA_ARGS__), X(64, 1, __VA_ARGS__), X(32, 3, __VA_ARGS__),   \
+        X(64, 2, __VA_ARGS__), X(64, 3, __VA_ARGS__), X(64, 4, __VA_ARGS__),                      \
+        X(512, 1, __VA_ARGS__), X(512, 2, __VA_ARGS__), X(512, 4, __VA_ARGS__),                   \
+        X(1024, 4, __VA_ARGS__), X(1024, 8, __VA_ARGS__)
+#define SP_LAYOUT_STRUCT(TPR, CPT, ...) Layout{TPR, CPT}
+constexpr Layout kLayouts[] = {SP_LAYOUT_LIST(SP_LAYOUT_STRUCT, 0)};
 constexpr int kNumLayouts = sizeof(kLayouts) / sizeof(kLayouts[0]);
 constexpr int kNumDefault = kNumLayouts;
 #ifndef SP_SUBWAVE_BLOCK
@@ -1039,18 +1031,23 @@ constexpr int block_of(int tpr) { return tpr <= kWave ? kSubWaveBlock : tpr; }
 #define SP_BWD_VARIANT -1
 #endif
 
-// Backward launch variants: (lanes per row, chunks per lane, row groups per
-// workgroup, rows in flight per row group, prefetch of the next step, workgroups
-// aimed for), the default choices in increasing capacity.
+// Backward launch variants: X(lanes per row, chunks per lane, row groups per
+// workgroup, rows in flight per row group, workgroups aimed for, ...).  The
+// first twelve are the default choices in increasing capacity; the last serves
+// the column schedule.  The host table and the kernel tables are both generated
+// from this list.
 struct BwdVariant {
-    int tpr, cpt, rg, pf, pipe, blocks;
+    int tpr, cpt, rg, pf, blocks;
 };
-constexpr BwdVariant kBwdVariants[] = {
-    {16, 1, 16, 1, 0, 256},  {32, 1, 8, 1, 0, 256},   {64, 1, 4, 1, 0, 256},   {32, 3, 8, 1, 0, 256},
-    {64, 2, 4, 1, 0, 256},   {64, 3, 4, 1, 0, 256},   {64, 4, 4, 1, 0, 256},   {512, 1, 1, 2, 0, 256},
-    {512, 2, 1, 1, 0, 512},  {512, 4, 1, 1, 0, 256},  {1024, 4, 1, 1, 0, 256}, {1024, 8, 1, 1, 0, 256},
-    {512, 1, 1, 4, 0, 256},
-};
+#define SP_BWD_LIST(X, ...)                                                                          \
+    X(16, 1, 16, 1, 256, __VA_ARGS__), X(32, 1, 8, 1, 256, __VA_ARGS__), X(64, 1, 4, 1, 256, __VA_ARGS__), \
+        X(32, 3, 8, 1, 256, __VA_ARGS__), X(64, 2, 4, 1, 256, __VA_ARGS__),                                \
+        X(64, 3, 4, 1, 256, __VA_ARGS__), X(64, 4, 4, 1, 256, __VA_ARGS__),                                \
+        X(512, 1, 1, 2, 256, __VA_ARGS__), X(512, 2, 1, 1, 512, __VA_ARGS__),                              \
+        X(512, 4, 1, 1, 256, __VA_ARGS__), X(1024, 4, 1, 1, 256, __VA_ARGS__),                             \
+        X(1024, 8, 1, 1, 256, __VA_ARGS__), X(512, 1, 1, 4, 256, __VA_ARGS__)
+#define SP_BWD_STRUCT(TPR, CPT, RG, PF, BLOCKS, ...) BwdVariant{TPR, CPT, RG, PF, BLOCKS}
+constexpr BwdVariant kBwdVariants[] = {SP_BWD_LIST(SP_BWD_STRUCT, 0)};
 constexpr int kNumBwdVariants = sizeof(kBwdVariants) / sizeof(kBwdVariants[0]);
 constexpr int kNumBwdDefault = 12;
 // Under the column schedule the (512, 1) rows take 4 rows in flight instead of 2.
@@ -1067,22 +1064,9 @@ constexpr int64_t kColRowBlocks = SP_COL_ROW_BLOCKS;
 typedef void (*FwdKernel)(FwdArgs);
 typedef void (*BwdKernel)(BwdArgs);
 
-#define SP_LAYOUT_LIST(X, ...)                                                                    \
-    X(16, 1, __VA_ARGS__), X(32, 1, __VA_ARGS__), X(64, 1, __VA_ARGS__), X(32, 3, __VA_ARGS__),   \
-        X(64, 2, __VA_ARGS__), X(64, 3, __VA_ARGS__), X(64, 4, __VA_ARGS__),                      \
-        X(512, 1, __VA_ARGS__), X(512, 2, __VA_ARGS__), X(512, 4, __VA_ARGS__),                   \
-        X(1024, 4, __VA_ARGS__), X(1024, 8, __VA_ARGS__)
-
 #define SP_FWD_ENTRY(TPR, CPT, DT, TT) &sp_fwd_kernel<DT, TT, TPR, CPT, block_of(TPR)>
-#define SP_BWD_LIST(X, ...)                                                                      \
-    X(16, 1, 16, 1, 0, __VA_ARGS__), X(32, 1, 8, 1, 0, __VA_ARGS__), X(64, 1, 4, 1, 0, __VA_ARGS__), \
-        X(32, 3, 8, 1, 0, __VA_ARGS__), X(64, 2, 4, 1, 0, __VA_ARGS__),                              \
-        X(64, 3, 4, 1, 0, __VA_ARGS__), X(64, 4, 4, 1, 0, __VA_ARGS__),                              \
-        X(512, 1, 1, 2, 0, __VA_ARGS__), X(512, 2, 1, 1, 0, __VA_ARGS__),                            \
-        X(512, 4, 1, 1, 0, __VA_ARGS__), X(1024, 4, 1, 1, 0, __VA_ARGS__),                           \
-        X(1024, 8, 1, 1, 0, __VA_ARGS__), X(512, 1, 1, 4, 0, __VA_ARGS__)
-#define SP_BWD_ENTRY(TPR, CPT, RG, PF, PIPE, DT, NORM, HDR, REGEN, COLS) \
-    &sp_bwd_kernel<DT, NORM, TPR, CPT, RG, PF, PIPE != 0, HDR, REGEN, COLS>
+#define SP_BWD_ENTRY(TPR, CPT, RG, PF, BLOCKS, DT, NORM, HDR, REGEN, COLS) \
+    &sp_bwd_kernel<DT, NORM, TPR, CPT, RG, PF, HDR, REGEN, COLS>
 
 const FwdKernel kFwdBf16[5][kNumLayouts] = {
     {SP_LAYOUT_LIST(SP_FWD_ENTRY, SP_BF16, 0)}, {SP_LAYOUT_LIST(SP_FWD_ENTRY, SP_BF16, 1)},
