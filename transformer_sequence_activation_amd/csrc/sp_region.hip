@@ -104,6 +104,9 @@ struct Act<SP_F32> {
 #ifndef SP_EARLY_FLAGS
 #define SP_EARLY_FLAGS 1  // forward with T <= 2: keep flags made while the loads are in flight
 #endif
+#ifndef SP_BWD_EARLY_FLAGS
+#define SP_BWD_EARLY_FLAGS 1  // mask-free backward, 2+ rows in flight: the same for its flags
+#endif
 __device__ __forceinline__ u32x4 ld16(const void* base, int64_t byte_off) {
     const u32x4* p = reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(base) + byte_off);
 #if SP_NT_LOADS
@@ -840,7 +843,30 @@ __global__ __launch_bounds__(RG* TPR) void sp_bwd_kernel(const BwdArgs a) {
     auto load_step = [&](int64_t r0, BwdRow<CPT, E>(&dst)[PF]) {
         bwd_load_step<DT, LN, CPT, PF, HAS_DR, REGEN, !COLS>(a, r0, row_end, col, dst);
     };
+    // regenerated keep flags (one bit per element), made right after a step's
+    // loads are issued so that the generator runs while they are in flight;
+    // measured to pay where several rows are in flight per row group
+    constexpr bool kEarly = REGEN && SP_BWD_EARLY_FLAGS && PF >= 2;
+    uint32_t kb[kEarly ? PF : 1][kEarly ? CPT : 1];
+    auto gen_flags = [&](int64_t r0) {
+        if constexpr (kEarly) {
+#pragma unroll
+            for (int p = 0; p < PF; ++p) {
+                const int64_t row = r0 + p;
+                const int64_t re = (row < row_end ? row : 0) * (int64_t)a.H;
+#pragma unroll
+                for (int k = 0; k < CPT; ++k) {
+                    bool kf[E];
+                    keep_flags<E>(a.base + (uint64_t)(re + col[k]), a.thr, a.key0, a.key1, kf);
+                    kb[p][k] = 0;
+#pragma unroll
+                    for (int e = 0; e < E; ++e) kb[p][k] |= (uint32_t)kf[e] << e;
+                }
+            }
+        }
+    };
     load_step(row_begin + (int64_t)rg * PF, rows);
+    gen_flags(row_begin + (int64_t)rg * PF);
     for (int it = 0; it < iters; ++it) {
         const int64_t row0 = row_begin + (int64_t)it * STEP + (int64_t)rg * PF;
         // pass 1: the two row sums of every row, and the dgamma / dbeta terms
@@ -888,10 +914,14 @@ __global__ __launch_bounds__(RG* TPR) void sp_bwd_kernel(const BwdArgs a) {
                 A::unpack(rows[p].hh[k], hv);
                 if constexpr (!kGammaRegs) load_vec_f32<E>(a.gamma, col[k], gk);
                 if constexpr (HAS_DR) A::unpack(rows[p].dr[k], drv);
-                if constexpr (REGEN)
+                if constexpr (kEarly) {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) keep[e] = (kb[p][k] >> e) & 1u;
+                } else if constexpr (REGEN) {
                     keep_flags<E>(a.base + (uint64_t)(row_elem + col[k]), a.thr, a.key0, a.key1, keep);
-                else
+                } else {
                     MW::unmake(rows[p].m[k], keep);
+                }
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
                     const float x = (hv[e] - rows[p].mu) * rows[p].rs;
@@ -908,7 +938,10 @@ __global__ __launch_bounds__(RG* TPR) void sp_bwd_kernel(const BwdArgs a) {
                 }
             }
         }
-        if (it + 1 < iters) load_step(row0 + STEP, rows);
+        if (it + 1 < iters) {
+            load_step(row0 + STEP, rows);
+            gen_flags(row0 + STEP);
+        }
     }
 
     // ---- this workgroup's partial dgamma / dbeta row ----
