@@ -112,7 +112,7 @@ class ShardBuffers:
         self.dbeta = torch.empty(H, device=dev) if ln else None
         self.desc = sp.make_desc(w.S, w.B, w.H, w.T, j, w.dtype, w.norm, w.eps, w.p, w.seed, flags)
         self.ws_bytes = max(16, sp.sp_region_bwd_workspace_size(self.desc))
-        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+        self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=dev)  # zero-filled once
 
     def prepare(self, sp, stream):
         self.fwd = sp.prepare_fwd(self.desc, self.P, self.res, self.gamma, self.beta, self.h, self.y,

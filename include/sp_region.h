@@ -143,14 +143,20 @@ int sp_region_fwd(const sp_desc_t* d, const void* const* P, const void* residual
  * d_residual, dP   shard outputs, activation type.
  * dgamma    [H] fp32, overwritten.  dbeta: [H] fp32 for LayerNorm, NULL for RMSNorm.
  * workspace device scratch of at least sp_region_bwd_workspace_size(d) bytes,
- *           16-byte aligned; contents on entry are ignored.  Calls that share a
- *           workspace must be ordered on one stream.  When that size is 0 the
- *           workspace is not touched and may be NULL.
+ *           16-byte aligned, zero-filled before the first call that uses it.
+ *           Its first 4096 bytes hold arrival counts that every call leaves at
+ *           zero again; the rest is scratch.  So one zero fill at allocation
+ *           serves every later call, for any descriptor, as long as only
+ *           sp_region_bwd writes the buffer.  Calls that share a workspace must
+ *           be ordered on one stream.  When that size is 0 the workspace is not
+ *           touched and may be NULL.
  *
  * dgamma / dbeta are fp32 sums in a fixed order, so repeated calls give the same
- * bits.  Two schedules exist, chosen from the shape: per-workgroup partial rows
- * in the workspace summed by a second kernel, or (short shards) workgroups that
- * each sum a strip of columns over all rows inside the one launch (no workspace).
+ * bits.  Two schedules exist, chosen from the shape (sp_region_bwd_schedule):
+ * per-workgroup partial rows in the workspace summed by a second kernel, or
+ * column workgroups inside the one launch, each summing a strip of columns over
+ * a segment of rows; where a strip has several segments, the workgroup that
+ * completes it adds them in segment order.
  */
 int sp_region_bwd(const sp_desc_t* d, const void* dY, const void* h, const uint8_t* mask,
                   const float* mean, const float* rstd, const float* gamma,
@@ -161,6 +167,12 @@ int sp_region_bwd(const sp_desc_t* d, const void* dY, const void* h, const uint8
 /* Bytes of workspace sp_region_bwd needs for this descriptor: 0 when it needs
  * none (then the workspace may be NULL) and on a bad descriptor. */
 size_t sp_region_bwd_workspace_size(const sp_desc_t* d);
+
+/* The dgamma / dbeta schedule sp_region_bwd takes for this descriptor: 0 =
+ * partial rows plus a finish kernel; k >= 1 = column workgroups with k row
+ * segments per strip (k = 1 needs no workspace); a negative status for a bad
+ * descriptor.  Host only; for tests and tuning. */
+int sp_region_bwd_schedule(const sp_desc_t* d);
 
 /*
  * Algorithmic HBM bytes of one call: every input read once and every output

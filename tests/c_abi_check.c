@@ -4,9 +4,11 @@
  * for device memory), and compares its forward and backward with the C oracle
  * (oracle/sp_oracle.c) on seeded inputs.
  *
- * Two shards are checked: a short LayerNorm shard (dgamma by column
- * workgroups, no workspace) and a long RMSNorm shard (partial rows and the
- * finish kernel, with a workspace).  Bar: mask and h byte-identical; y,
+ * Three shards are checked, one per dgamma schedule: a short LayerNorm shard
+ * (column workgroups, one row segment, no workspace), a 1024-row RMSNorm shard
+ * (column workgroups over several row segments, called twice on the one
+ * zero-filled workspace: the second call must give the same bits) and a long
+ * RMSNorm shard (partial rows and the finish kernel).  Bar: mask and h byte-identical; y,
  * d_residual, dP, dgamma, dbeta within 1e-2 relative (plus 1e-2 of the rms of
  * the reference); rstd and mean within 1e-5.  Exit status 0 = pass.
  * --any-schedule: do not check which dgamma schedule each shard gets.
@@ -104,7 +106,8 @@ static void* dev_copy(const void* host, size_t bytes)
     return d;
 }
 
-static void check_shard(int64_t S, int64_t B, int64_t H, int32_t T, int32_t j, int32_t norm, int expect_ws)
+/* expect: 0 = partial rows, 1 = column workgroups with one row segment, 2 = with several */
+static void check_shard(int64_t S, int64_t B, int64_t H, int32_t T, int32_t j, int32_t norm, int expect)
 {
     const int ln = norm == SP_LAYERNORM;
     const int64_t R = (S / T) * B, N = R * H, full = S * B * H;
@@ -114,14 +117,14 @@ static void check_shard(int64_t S, int64_t B, int64_t H, int32_t T, int32_t j, i
     spo_desc od;
     uint16_t *Ph[SP_MAX_T], *res, *dY, *h_g, *y_g, *h_o, *y_o, *dres_g, *dP_g, *dres_o, *dP_o;
     uint8_t *m_g, *m_o;
-    float *gam, *bet, *rs_g, *mu_g, *dgam_g, *dbet_g;
+    float *gam, *bet, *rs_g, *mu_g, *dgam_g, *dbet_g, *dgam_first = NULL;
     double *gam64, *bet64, *rs_o, *mu_o, *rs_o32, *mu_o32, *dgam_o, *dbet_o, *a, *b;
     void *Pd[SP_MAX_T], *res_d, *dY_d, *gam_d, *bet_d, *h_d, *y_d, *m_d, *mu_d, *rs_d;
     void *dres_d, *dP_d, *dgam_d, *dbet_d, *ws_d = NULL;
     const void* Pshard[SP_MAX_T];
     size_t ws;
     int64_t i;
-    int t, rc;
+    int t, rc, sched;
 
     printf("[case] S=%lld B=%lld H=%lld T=%d j=%d %s\n", (long long)S, (long long)B, (long long)H, T, j,
            ln ? "LayerNorm" : "RMSNorm");
@@ -176,20 +179,34 @@ static void check_shard(int64_t S, int64_t B, int64_t H, int32_t T, int32_t j, i
         return;
     }
     ws = sp_region_bwd_workspace_size(&d);
-    if (!any_schedule && (ws > 0) != expect_ws) {
-        fprintf(stderr, "  workspace of %zu bytes, expected %s\n", ws, expect_ws ? "some" : "none");
+    sched = sp_region_bwd_schedule(&d);
+    if (sched < 0 || (sched == 1) != (ws == 0)) {
+        fprintf(stderr, "  schedule %d with a workspace of %zu bytes\n", sched, ws);
         ++failures;
     }
-    if (ws > 0) CHECK_HIP(hipMalloc(&ws_d, ws));
-    rc = sp_region_bwd(&d, dY_d, h_d, (const uint8_t*)m_d, ln ? (const float*)mu_d : NULL, (const float*)rs_d,
-                       (const float*)gam_d, NULL, dres_d, dP_d, (float*)dgam_d, ln ? (float*)dbet_d : NULL, ws_d,
-                       ws, NULL);
-    if (rc != SP_OK) {
-        fprintf(stderr, "  sp_region_bwd: %s\n", sp_region_strerror(rc));
+    if (!any_schedule && (sched > 2 ? 2 : sched) != expect) {
+        fprintf(stderr, "  dgamma schedule %d, expected %d\n", sched, expect);
         ++failures;
-        return;
     }
-    CHECK_HIP(hipDeviceSynchronize());
+    if (ws > 0) {
+        CHECK_HIP(hipMalloc(&ws_d, ws));
+        CHECK_HIP(hipMemset(ws_d, 0, ws));
+    }
+    for (t = 0; t < 2; ++t) {  /* twice on one workspace: the second call must repeat the first */
+        rc = sp_region_bwd(&d, dY_d, h_d, (const uint8_t*)m_d, ln ? (const float*)mu_d : NULL,
+                           (const float*)rs_d, (const float*)gam_d, NULL, dres_d, dP_d, (float*)dgam_d,
+                           ln ? (float*)dbet_d : NULL, ws_d, ws, NULL);
+        if (rc != SP_OK) {
+            fprintf(stderr, "  sp_region_bwd: %s\n", sp_region_strerror(rc));
+            ++failures;
+            return;
+        }
+        CHECK_HIP(hipDeviceSynchronize());
+        if (t == 0) {
+            dgam_first = (float*)malloc((size_t)H * 4);
+            CHECK_HIP(hipMemcpy(dgam_first, dgam_d, (size_t)H * 4, hipMemcpyDeviceToHost));
+        }
+    }
     h_g = (uint16_t*)malloc((size_t)N * 2);
     y_g = (uint16_t*)malloc((size_t)N * 2);
     dres_g = (uint16_t*)malloc((size_t)N * 2);
@@ -208,6 +225,10 @@ static void check_shard(int64_t S, int64_t B, int64_t H, int32_t T, int32_t j, i
     CHECK_HIP(hipMemcpy(dP_g, dP_d, (size_t)N * 2, hipMemcpyDeviceToHost));
     CHECK_HIP(hipMemcpy(dgam_g, dgam_d, (size_t)H * 4, hipMemcpyDeviceToHost));
     CHECK_HIP(hipMemcpy(dbet_g, dbet_d, (size_t)H * 4, hipMemcpyDeviceToHost));
+    if (memcmp(dgam_first, dgam_g, (size_t)H * 4) != 0) {
+        fprintf(stderr, "  dgamma of the second call on the workspace differs from the first\n");
+        ++failures;
+    }
 
     /* the oracle, on the shard's rows */
     for (t = 0; t < T; ++t) Pshard[t] = Ph[t] + (int64_t)j * N;
@@ -283,7 +304,7 @@ static void check_shard(int64_t S, int64_t B, int64_t H, int32_t T, int32_t j, i
     CHECK_HIP(hipFree(dgam_d)); CHECK_HIP(hipFree(dbet_d));
     if (ws_d) CHECK_HIP(hipFree(ws_d));
     free(res); free(dY); free(gam); free(bet); free(gam64); free(bet64);
-    free(h_g); free(y_g); free(dres_g); free(dP_g); free(m_g); free(rs_g); free(mu_g); free(dgam_g); free(dbet_g);
+    free(h_g); free(y_g); free(dres_g); free(dP_g); free(m_g); free(rs_g); free(mu_g); free(dgam_g); free(dbet_g); free(dgam_first);
     free(h_o); free(y_o); free(m_o); free(rs_o); free(mu_o); free(rs_o32); free(mu_o32);
     free(dres_o); free(dP_o); free(dgam_o); free(dbet_o); free(a); free(b);
 }
@@ -306,8 +327,9 @@ int main(int argc, char** argv)
         fprintf(stderr, "S %% T != 0 was not reported as SP_ESHAPE\n");
         return 1;
     }
-    check_shard(64, 2, 256, 2, 1, SP_LAYERNORM, 0);   /* 64 rows: column dgamma, no workspace */
-    check_shard(2048, 1, 256, 4, 2, SP_RMSNORM, 1);   /* 512 rows: partial rows + finish */
+    check_shard(64, 2, 256, 2, 1, SP_LAYERNORM, 1);    /* 64 rows: columns, one segment */
+    check_shard(2048, 1, 1024, 2, 1, SP_RMSNORM, 2);   /* 1024 rows: columns, four segments */
+    check_shard(16384, 1, 1024, 2, 1, SP_RMSNORM, 0);  /* 8192 rows: partial rows + finish */
     if (failures) {
         fprintf(stderr, "c_abi_check: %d failure(s)\n", failures);
         return 1;

@@ -191,7 +191,7 @@ def test_fwd_empty_shard_is_a_noop(lib):
 
 def rows_desc(**kw):
     """A shard long enough for the partial-row schedule (it needs a workspace)."""
-    base = dict(S=2048, B=1, H=256, T=4, j=1)
+    base = dict(S=16384, B=1, H=1024, T=2, j=1)
     base.update(kw)
     return good_desc(**base)
 
@@ -233,35 +233,52 @@ def test_traffic_bytes_follow_the_accounting(lib):
 
 
 def test_workspace_size_scales_with_norm(lib):
-    rms = sp.sp_region_bwd_workspace_size(rows_desc(norm="rms"))
-    ln = sp.sp_region_bwd_workspace_size(rows_desc(norm="ln"))
-    assert ln == 2 * rms and rms % 16 == 0
+    # 4096 bytes of arrival counts, then partial sums: twice as many for LayerNorm
+    for d in (rows_desc, lambda **kw: good_desc(S=2048, B=2, H=2048, T=2, **kw)):
+        rms = sp.sp_region_bwd_workspace_size(d(norm="rms"))
+        ln = sp.sp_region_bwd_workspace_size(d(norm="ln"))
+        assert ln - rms == rms - 4096 > 0 and rms % 16 == 0
     assert sp.sp_region_bwd_workspace_size(good_desc(S=0)) == 0
 
 
-@pytest.mark.parametrize("shape,uses_workspace", [
-    # (S, B, H, T, dtype, norm): short shards sum dgamma by columns (no workspace)
-    ((4096, 1, 4096, 8, "bf16", "ln"), False),   # the LayerNorm T=8 shard, 512 rows
-    ((4080, 1, 4096, 8, "bf16", "ln"), False),   # 510 rows
-    ((4112, 1, 4096, 8, "bf16", "ln"), True),    # 514 rows: past one batch of a column lane
-    ((400, 3, 2056, 4, "bf16", "ln"), False),    # 300 rows, a ragged last strip
-    ((40, 5, 2000, 2, "f32", "ln"), False),
-    ((256, 1, 64, 2, "f32", "rms"), False),
-    ((8192, 2, 8192, 8, "bf16", "rms"), True),   # 2048 rows of 8192
-    ((2048, 2, 768, 2, "bf16", "rms"), True),    # 2048 rows of 768
-    ((32768, 1, 8192, 8, "bf16", "rms"), True),
-    ((4096, 4, 128, 4, "bf16", "ln"), True),     # 4096 short rows
-    ((16, 2, 20480, 4, "bf16", "ln"), False),    # 8 long rows (1024-lane workgroups)
-    ((1040, 1, 20480, 2, "bf16", "rms"), True),  # 520 long rows: past the 512-row column limit
-    ((1040, 1, 65536, 2, "bf16", "ln"), True),
+@pytest.mark.parametrize("shape,schedule", [
+    # (S, B, H, T, dtype, norm) -> 0 = partial rows + finish kernel; k >= 1 = column
+    # workgroups with k row segments per strip (k = 1: no workspace)
+    ((4096, 1, 4096, 8, "bf16", "ln"), 1),     # the LayerNorm T=8 shard, 512 rows
+    ((4080, 1, 4096, 8, "bf16", "ln"), 1),     # 510 rows
+    ((4112, 1, 4096, 8, "bf16", "ln"), 2),     # 514 rows: past one batch of a column lane
+    ((400, 3, 2056, 4, "bf16", "ln"), 1),      # 300 rows, a ragged last strip
+    ((40, 5, 2000, 2, "f32", "ln"), 1),
+    ((256, 1, 64, 2, "f32", "rms"), 1),
+    ((8192, 2, 8192, 8, "bf16", "rms"), 0),    # 2048 rows of 8192
+    ((2048, 2, 768, 2, "bf16", "rms"), 0),     # 2048 rows of 768: small partial rows
+    ((32768, 1, 8192, 8, "bf16", "rms"), 0),
+    ((4096, 4, 128, 4, "bf16", "ln"), 0),      # 4096 short rows
+    ((16384, 1, 1024, 2, "bf16", "rms"), 0),   # 8192 rows of 1024
+    ((16, 2, 20480, 4, "bf16", "ln"), 1),      # 8 long rows (1024-lane workgroups)
+    ((8192, 1, 4096, 8, "bf16", "ln"), 2),     # 1024 rows of 4096: 2 segments of 512
+    ((2048, 2, 2048, 2, "bf16", "rms"), 8),    # 2048 rows of 2048: 8 segments of 256
+    ((2056, 1, 2056, 2, "bf16", "ln"), 3),     # 1028 rows, a ragged last strip
+    ((4100, 1, 1024, 2, "f32", "ln"), 9),      # 2050 fp32 rows: 9 segments of 228
+    ((1040, 1, 20480, 2, "bf16", "rms"), 0),   # 520 long rows: 1024-lane columns would spill
+    ((1040, 1, 65536, 2, "bf16", "ln"), 2),    # 520 of the longest rows: partial rows too large
 ])
-def test_backward_schedule_by_shape(lib, shape, uses_workspace):
-    """Both dgamma schedules are exercised by the GPU parity shapes listed here."""
+def test_backward_schedule_by_shape(lib, shape, schedule):
+    """Every dgamma schedule is exercised by the GPU parity shapes listed here."""
     S, B, H, T, dtype, norm = shape
     d = sp.make_desc(S, B, H, T, 1, dtype, norm)
+    assert sp.sp_region_bwd_schedule(d) == schedule
     need = sp.sp_region_bwd_workspace_size(d)
-    assert (need > 0) == uses_workspace
-    if not uses_workspace:
+    assert (need == 0) == (schedule == 1)
+    if schedule == 1:
         # no workspace needed: validation still catches every other error
         assert bwd_call(d, workspace=None, ws_bytes=0, dY=None) == -1
         assert bwd_call(d, workspace=None, ws_bytes=0, dgamma=fake(2)) == -1  # dgamma over h
+    else:
+        assert bwd_call(d, workspace=None) == -6
+
+
+def test_schedule_of_a_bad_descriptor(lib):
+    assert lib.sp_region_bwd_schedule(None) == -1
+    assert sp.sp_region_bwd_schedule(good_desc(S=66)) == -2
+    assert sp.sp_region_bwd_schedule(good_desc(S=0)) == 0

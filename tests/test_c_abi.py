@@ -3,8 +3,9 @@ include/sp_region.h and the HIP runtime API, compared with the C oracle.
 
 CPU: it compiles as strict C99 with every warning an error (the header is
 valid C) and links against libsp_region.so and the oracle.
-GPU: it runs, on a short LayerNorm shard (column dgamma) and a long RMSNorm
-shard (partial rows), and matches the oracle.
+GPU: it runs, on a short LayerNorm shard (column dgamma), a 1024-row RMSNorm
+shard (column dgamma over four row segments) and a long RMSNorm shard (partial
+rows), and matches the oracle.
 """
 import os
 import subprocess
@@ -44,8 +45,9 @@ def test_c_program_matches_the_oracle(tmp_path):
 
     exe = build_check(tmp_path)
     # a tuning build may force one dgamma schedule for every shape; the default
-    # build gives the long shard a workspace (partial rows)
-    forced = sp.sp_region_bwd_workspace_size(sp.make_desc(2048, 1, 256, 4, 2, "bf16", "rms")) == 0
+    # build sums the short shard by columns and the long one by partial rows
+    forced = (sp.sp_region_bwd_schedule(sp.make_desc(64, 2, 256, 2, 1, "bf16", "ln")) != 1 or
+              sp.sp_region_bwd_schedule(sp.make_desc(16384, 1, 1024, 2, 1, "bf16", "rms")) != 0)
     print("\n[case] tests/c_abi_check.c on the GPU", flush=True)
     r = subprocess.run([exe] + (["--any-schedule"] if forced else []), capture_output=True, text=True,
                        timeout=120)

@@ -351,10 +351,13 @@ EDGE = [
     (4, 16, 2, 20480, "bf16", "ln", 0.1, 1),    # 2560-chunk rows: 1024 lanes x 4 chunks, in batches
     (3, 6, 1, 20480, "bf16", "rms", 0.2, 2),    # the same with a run-time T
     (2, 8, 1, 10240, "f32", "rms", 0.1, 0),     # fp32, 2560-chunk rows
-    (2, 1040, 1, 20480, "bf16", "rms", 0.1, 1), # 520 long rows: partial rows, 1024 lanes x 4 chunks
-    (2, 1040, 1, 65536, "bf16", "ln", 0.1, 0),  # 520 of the longest rows: partial rows, 8 chunks
+    (2, 1040, 1, 20480, "bf16", "rms", 0.1, 1), # 520 long rows, 1024 lanes x 4 chunks
+    (2, 1040, 1, 65536, "bf16", "ln", 0.1, 0),  # 520 of the longest rows, 8 chunks
     (8, 4080, 1, 4096, "bf16", "ln", 0.1, 2),   # 510 rows: column dgamma, ragged last 4-row tile
-    (8, 4112, 1, 4096, "bf16", "ln", 0.1, 6),   # 514 rows: just past the column limit, partial rows
+    (8, 4112, 1, 4096, "bf16", "ln", 0.1, 6),   # 514 rows: two column segments of 257 rows
+    (2, 2056, 1, 2056, "bf16", "ln", 0.3, 1),   # 1028 rows: 3 column segments, ragged strip
+    (2, 4100, 1, 1024, "f32", "ln", 0.1, 1),    # 2050 fp32 rows: 9 column segments of 228
+    (2, 16384, 1, 1024, "bf16", "ln", 0.1, 0),  # 8192 rows: partial rows + finish kernel
 ]
 
 
@@ -474,15 +477,23 @@ def test_gpu_argument_errors_leave_outputs_untouched():
     assert bool((h == 3).all()) and bool((y == 3).all()) and bool((m == 3).all())
 
 
-@pytest.mark.parametrize("name,j", [("minimind_T2_S2048_B2_H768", 1), ("layernorm_T8_S4096_B1_H4096", 3)])
-def test_graph_replays_match_eager(name, j):
+ROWS_SHARD = W.Workload("rows_T2_S16384_B1_H1024", 940, 2, 16384, 1, 1024, "bf16", "rms", 1e-6, 0.1, (1,))
+SEG8_SHARD = W.Workload("seg8_T2_S2048_B2_H2048", 942, 2, 2048, 2, 2048, "bf16", "rms", 1e-6, 0.1, (1,))
+
+
+@pytest.mark.parametrize("w,j,schedule", [(SEG8_SHARD, 1, 8),
+                                          (W.WORKLOADS["layernorm_T8_S4096_B1_H4096"], 3, 1),
+                                          (ROWS_SHARD, 1, 0)], ids=lambda v: getattr(v, "name", str(v)))
+def test_graph_replays_match_eager(w, j, schedule):
     """The library enqueues kernels only (no memset, no allocation), so a HIP
     graph of forward + backward replays to the eager results every time, with
-    the program's own eager work between replays.  The two shards use the two
-    dgamma schedules (partial rows + finish kernel; column workgroups)."""
-    print(f"\n[case] {name} shard {j}: HIP graph capture of forward + backward, three replays",
+    the program's own eager work between replays.  The three shards take the
+    three dgamma schedules (column workgroups over 8 row segments, whose
+    arrival counts must return to zero after every replay; column workgroups
+    over all rows; partial rows + finish kernel)."""
+    print(f"\n[case] {w.name} shard {j}: HIP graph capture of forward + backward, three replays",
           flush=True)
-    w = W.WORKLOADS[name]
+    assert sp.sp_region_bwd_schedule(gdesc(w, j)) == schedule
     c = Case(w, "cpu")
     d = gdesc(w, j)
     ln = w.norm == "ln"
@@ -492,7 +503,7 @@ def test_graph_replays_match_eager(name, j):
     fk = ("h", "y", "mask", "rstd") + (("mean",) if ln else ())
     bk = ("d_res", "dP", "dgamma") + (("dbeta",) if ln else ())
     ref = {**{k: f[k].clone() for k in fk}, **{k: b[k].clone() for k in bk}}
-    ws = torch.empty(max(16, sp.sp_region_bwd_workspace_size(d)), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(16, sp.sp_region_bwd_workspace_size(d)), dtype=torch.uint8, device="cuda")
     s = torch.cuda.Stream()
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
@@ -515,6 +526,30 @@ def test_graph_replays_match_eager(name, j):
         for k in ref:
             assert torch.equal(ref[k], got[k]), (rep, k)
         del other
+
+
+def test_workspace_reused_across_calls_and_shapes():
+    """One workspace, zero-filled once, serves calls of every schedule in turn:
+    each call gives the bits of the same call on a fresh workspace."""
+    print("\n[case] one workspace for partial rows, then 8 and 2 column segments, twice", flush=True)
+    cases = [(ROWS_SHARD, 1), (SEG8_SHARD, 0),
+             (W.Workload("seg2_T8_S4112_B1_H4096", 941, 8, 4112, 1, 4096, "bf16", "ln", 1e-5, 0.1, (6,)), 6)]
+    runs = []
+    for w, j in cases:
+        c = Case(w, "cuda")
+        f = gpu_fwd(c, j)
+        runs.append((c, j, f, gpu_bwd(c, j, f)))  # fresh zero-filled workspace
+    need = max(sp.sp_region_bwd_workspace_size(gdesc(c.w, j)) for c, j, _, _ in runs)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for rep in range(2):
+        for c, j, f, ref in runs:
+            got = sp.backward(gdesc(c.w, j), c.shard(c.dY, j), f["h"], f["mask"], f["mean"], f["rstd"],
+                              c.gamma, workspace=ws)
+            torch.cuda.synchronize()
+            for k in ("d_res", "dP", "dgamma") + (("dbeta",) if c.w.norm == "ln" else ()):
+                assert torch.equal(ref[k], got[k]), (rep, c.w.name, k)
+    counts = ws[:4096]
+    assert not bool(counts.any())  # every call left its arrival counts at zero
 
 
 @pytest.mark.parametrize("name,j", [("layernorm_T8_S4096_B1_H4096", 3), ("minimind_T2_S2048_B2_H768", 1)])

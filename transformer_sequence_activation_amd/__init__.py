@@ -23,7 +23,8 @@ SP_OK = 0
 STATUS = {0: "SP_OK", -1: "SP_EINVAL", -2: "SP_ESHAPE", -3: "SP_EDTYPE", -4: "SP_EPARAM",
           -5: "SP_EALIGN", -6: "SP_EWORKSPACE", -7: "SP_EHIP"}
 EXPORTED = ("sp_region_fwd", "sp_region_bwd", "sp_region_bwd_workspace_size",
-            "sp_region_traffic_bytes", "sp_region_strerror", "sp_region_version")
+            "sp_region_bwd_schedule", "sp_region_traffic_bytes", "sp_region_strerror",
+            "sp_region_version")
 
 
 class SpDesc(ctypes.Structure):
@@ -68,6 +69,8 @@ def load(path=LIB_PATH):
     L.sp_region_bwd.restype = ctypes.c_int
     L.sp_region_bwd_workspace_size.argtypes = [pdesc]
     L.sp_region_bwd_workspace_size.restype = sz
+    L.sp_region_bwd_schedule.argtypes = [pdesc]
+    L.sp_region_bwd_schedule.restype = ctypes.c_int
     L.sp_region_traffic_bytes.argtypes = [pdesc, ctypes.POINTER(ctypes.c_uint64),
                                           ctypes.POINTER(ctypes.c_uint64)]
     L.sp_region_traffic_bytes.restype = ctypes.c_int
@@ -128,6 +131,12 @@ def sp_region_bwd_workspace_size(desc):
     return load().sp_region_bwd_workspace_size(ctypes.byref(desc))
 
 
+def sp_region_bwd_schedule(desc):
+    """0 = partial rows + finish kernel; k >= 1 = column workgroups with k row
+    segments per strip; negative = status of a bad descriptor."""
+    return load().sp_region_bwd_schedule(ctypes.byref(desc))
+
+
 def sp_region_fwd(desc, P, residual, gamma, beta, h_out, y_out, mask_out, mean_out, rstd_out,
                   stream=None):
     """Returns the status code (0 = success); see include/sp_region.h."""
@@ -175,14 +184,15 @@ def forward(desc, P, residual, gamma, beta=None, stream=None):
 
 
 def backward(desc, dY, h, mask, mean, rstd, gamma, dR=None, workspace=None, stream=None):
-    """Returns dict d_res, dP, dgamma, dbeta (None for RMSNorm)."""
+    """Returns dict d_res, dP, dgamma, dbeta (None for RMSNorm).  A workspace
+    passed in must have been zero-filled before its first use."""
     import torch
     dev = dY.device
     R, H = desc.R, desc.H
     act = _act_dtype(desc)
     ws_bytes = sp_region_bwd_workspace_size(desc)
     if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+        workspace = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     out = {
         "d_res": torch.empty((R, H), dtype=act, device=dev),
         "dP": torch.empty((R, H), dtype=act, device=dev),

@@ -619,7 +619,9 @@ struct BwdArgs {
     const void* dR;
     void* dres;
     void* dP;
-    float* ws;            // [G][nacc][H] fp32 partial sums of dgamma (, dbeta)
+    float* ws;            // [G][nacc][H] fp32 partial sums of dgamma (, dbeta) per row workgroup,
+                          // or [segments][nacc][H] per column segment
+    uint32_t* col_count;  // [strips] arrivals of a strip's column segments, zero between calls
     float* dgamma;        // [H] outputs, written directly by the column workgroups
     float* dbeta;
     uint64_t base;        // global index of the shard's first element (mask regeneration)
@@ -631,6 +633,8 @@ struct BwdArgs {
     int32_t norm;
     int32_t nacc;         // 1 (RMSNorm) or 2 (LayerNorm)
     int32_t col_blocks;   // leading workgroups that sum dgamma / dbeta by columns (0 = partial rows)
+    int32_t col_strips;   // column strips; col_blocks / col_strips segments of rows per strip
+    int64_t col_seg_rows; // rows per segment
     float scale;
     float inv_h;
 };
@@ -677,13 +681,17 @@ __device__ __forceinline__ void bwd_load_step(const BwdArgs& a, int64_t row0, in
     }
 }
 
-// dgamma / dbeta by columns.  Workgroup `strip` owns kSeg adjacent 16-byte
-// chunks (128 bytes of every row, lanes kSeg apart share a chunk) and sums
-// dY * xhat (and dY) over all R rows of the shard: its BLOCK / kSeg row offsets
-// each take every (BLOCK / kSeg)-th row in ascending order, then the offsets
-// are added in a fixed tree (lane butterfly inside a wavefront, wavefronts in
-// order through LDS).  Needs no partial rows and no second launch, at the cost
-// of reading dY and h a second time.
+// dgamma / dbeta by columns.  A column workgroup owns one strip of kSeg adjacent
+// 16-byte chunks (128 bytes of every row, lanes kSeg apart share a chunk) and
+// one segment of contiguous rows, and sums dY * xhat (and dY) over them: its
+// BLOCK / kSeg row offsets each take every (BLOCK / kSeg)-th row in ascending
+// order, then the offsets are added in a fixed tree (lane butterfly inside a
+// wavefront, wavefronts in order through LDS).  With one segment per strip
+// that sum is dgamma.  With several, each segment publishes its sums and counts
+// itself in; the workgroup that completes the strip adds the segments in
+// segment order and sets the count back to zero.  The order of every addition
+// is fixed, whichever workgroup finishes last.  Needs no second launch, at the
+// cost of reading dY and h a second time.
 #ifndef SP_COL_BATCH
 #define SP_COL_BATCH 8
 #endif
@@ -697,7 +705,7 @@ constexpr int col_batch(int block) { return block > 512 ? (kColBatch + 1) / 2 : 
 constexpr int kSeg = SP_COL_SEG;  // lanes per row segment (16 bytes each)
 
 template <int DT, bool LN, int BLOCK>
-__device__ __forceinline__ void bwd_columns(const BwdArgs& a, int strip) {
+__device__ __forceinline__ void bwd_columns(const BwdArgs& a, int wg) {
     using A = Act<DT>;
     constexpr int E = A::E;
     constexpr int EB = A::kBytes;
@@ -706,7 +714,13 @@ __device__ __forceinline__ void bwd_columns(const BwdArgs& a, int strip) {
     constexpr int kB = col_batch(BLOCK);  // steps whose loads are in flight together
     constexpr int NW = BLOCK / kWave;
     __shared__ float cred[NW][NACC][kSeg * E];
+    __shared__ uint32_t completes;
 
+    const int strip = wg % a.col_strips;
+    const int seg = wg / a.col_strips;
+    const int nseg = a.col_blocks / a.col_strips;
+    const int64_t row_lo = (int64_t)seg * a.col_seg_rows;
+    const int64_t row_hi = min(row_lo + a.col_seg_rows, a.R);
     const int tid = threadIdx.x;
     const int ch = tid % kSeg;
     const int ro = tid / kSeg;
@@ -719,15 +733,15 @@ __device__ __forceinline__ void bwd_columns(const BwdArgs& a, int strip) {
         dg[e] = 0.0f;
         db[e] = 0.0f;
     }
-    for (int64_t r0 = 0; r0 < a.R; r0 += (int64_t)kRO * kB) {
+    for (int64_t r0 = row_lo; r0 < row_hi; r0 += (int64_t)kRO * kB) {
         u32x4 dy[kB], hh[kB];
         float mu[kB], rs[kB];
         bool rok[kB];
 #pragma unroll
         for (int b = 0; b < kB; ++b) {
             const int64_t row = r0 + (int64_t)b * kRO + ro;
-            rok[b] = row < a.R;
-            const int64_t rr = rok[b] ? row : a.R - 1;
+            rok[b] = row < row_hi;
+            const int64_t rr = rok[b] ? row : row_hi - 1;
             const int64_t off = (rr * a.H + col) * EB;
             dy[b] = ld16_col(a.dY, off);
             hh[b] = ld16_col(a.h, off);
@@ -767,15 +781,49 @@ __device__ __forceinline__ void bwd_columns(const BwdArgs& a, int strip) {
         }
     }
     __syncthreads();
-    if (tid < NACC * kSeg * E) {
-        const int acc = tid / (kSeg * E);
+    const bool mine = tid < NACC * kSeg * E;
+    const int acc = tid / (kSeg * E);
+    const int gcol = strip * kSeg * E + tid % (kSeg * E);
+    const bool live = mine && gcol < a.H;
+    float v = 0.0f;
+    if (mine) {
         const int cc = tid % (kSeg * E);
-        float v = cred[0][acc][cc];
+        v = cred[0][acc][cc];
 #pragma unroll
         for (int q = 1; q < NW; ++q) v += cred[q][acc][cc];
-        const int gcol = strip * kSeg * E + cc;
-        if (gcol < a.H) (acc == 0 ? a.dgamma : a.dbeta)[gcol] = v;
     }
+    float* const out = acc == 0 ? a.dgamma : a.dbeta;
+    if (nseg == 1) {  // uniform over the grid
+        if (live) out[gcol] = v;
+        return;
+    }
+    // Several segments: publish this one's sums, then count in.  The sums go
+    // out as device-scope stores, which are coherent across the XCDs' L2
+    // caches once complete; every wave drains its stores before the barrier,
+    // so they are complete before the count is taken, and the workgroup that
+    // completes the strip reads them back with device-scope loads.  (A device
+    // fence would instead write back every dirty line of the L2, the
+    // d_residual and dP tiles of the whole XCD included: measured 20 vs 8 us.)
+    float* const part = a.ws + ((int64_t)seg * NACC + acc) * a.H + gcol;
+    if (live) __hip_atomic_store(part, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t before = atomicAdd(a.col_count + strip, 1u);
+        completes = before == (uint32_t)(nseg - 1);
+    }
+    __syncthreads();
+    if (!completes) return;  // uniform over the workgroup
+    if (live) {
+        const float* src = a.ws + (int64_t)acc * a.H + gcol;
+        float t = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int q = 1; q < nseg; ++q)
+            t += __hip_atomic_load(src + (int64_t)q * NACC * a.H, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        out[gcol] = t;
+    }
+    // every segment of this strip has counted in: no other workgroup of the
+    // launch touches the count again
+    if (tid == 0) __hip_atomic_store(a.col_count + strip, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // A workgroup holds RG row groups of TPR lanes and walks a tile of
@@ -1089,10 +1137,16 @@ static_assert(kBwdVariants[kBwdCol512From].tpr == 512 && kBwdVariants[kBwdCol512
                   kBwdVariants[kBwdCol512To].tpr == 512 && kBwdVariants[kBwdCol512To].cpt == 1 &&
                   kBwdVariants[kBwdCol512To].rg == kBwdVariants[kBwdCol512From].rg,
               "the column-schedule swap keeps the row layout and block size");
+#ifndef SP_COL_MIN_SEGS
+#define SP_COL_MIN_SEGS 1  // row segments per column strip at least (tuning)
+#endif
 #ifndef SP_COL_ROW_BLOCKS
 #define SP_COL_ROW_BLOCKS 256  // row + column workgroups the column schedule aims for
 #endif
-constexpr int64_t kColRowBlocks = SP_COL_ROW_BLOCKS;
+#ifndef SP_COL_ROW_BLOCKS_SMALL
+#define SP_COL_ROW_BLOCKS_SMALL 256  // the same for workgroups of 256 lanes or fewer
+#endif
+constexpr int64_t col_row_blocks(int block) { return block <= 256 ? SP_COL_ROW_BLOCKS_SMALL : SP_COL_ROW_BLOCKS; }
 
 typedef void (*FwdKernel)(FwdArgs);
 typedef void (*BwdKernel)(BwdArgs);
@@ -1206,8 +1260,16 @@ struct BwdPlan {
     int nacc;
     size_t ws_bytes;
     size_t lds_bytes;
-    int64_t col_blocks;  // > 0: dgamma / dbeta by column workgroups, no workspace, no finish
+    int64_t col_blocks;  // > 0: dgamma / dbeta by column workgroups, no finish launch
+    int64_t col_strips;
+    int64_t col_seg_rows;
 };
+
+// A workspace starts with one arrival count per column strip (zero between
+// calls, written only by column segments); partial sums follow.
+constexpr size_t kWsCountBytes = 4096;
+static_assert((size_t)SP_MAX_H_BYTES / 16 / kSeg * sizeof(uint32_t) <= kWsCountBytes,
+              "a count for every strip of the longest row");
 
 // dgamma / dbeta strategy: 0 = by estimated bytes, 1 = partial rows + finish
 // kernel, 2 = column workgroups.
@@ -1217,15 +1279,27 @@ struct BwdPlan {
 // The finish launch costs about as much time as moving this many bytes.
 constexpr int64_t kFinishLaunchBytes = (int64_t)16 << 20;
 
+// Rows a column workgroup takes in one batch of loads: one segment at most, so
+// that no column walk becomes the critical path of the launch.
+constexpr int64_t col_segment_rows(int block) { return (int64_t)(block / kSeg) * col_batch(block); }
+
+// Partial rows smaller than this are cheaper than the arrival chain of
+// several column segments (store, count, read back).
+constexpr int64_t kSegMinPartialBytes = (int64_t)2 << 20;
+
 // Column workgroups read dY and h a second time (2 R H e bytes) but need no
 // partial rows (2 G nacc H 4 bytes written and read back) and no second launch.
-// They are used only where each of their lanes issues all of its loads in one
-// batch: a longer column walk becomes the critical path of the launch.
+// Rows past one segment add the segments' arrival chain, which costs about as
+// much as the finish launch: several segments pay only where the partial rows
+// are large, and 1024-lane column workgroups (long rows, whose registers spill)
+// get no credit for the launch they save.
 bool use_columns(int64_t R, int64_t H, int eb, int64_t G, int nacc, int block) {
     if (SP_BWD_DG == 1 || R == 0) return false;
     if (SP_BWD_DG == 2) return true;
-    if (R > (int64_t)(block / kSeg) * col_batch(block)) return false;
-    return 2 * R * H * eb <= 2 * G * nacc * H * 4 + kFinishLaunchBytes;
+    const int64_t reread = 2 * R * H * eb, partial = 2 * G * nacc * H * 4;
+    if (R <= col_segment_rows(block)) return reread <= partial + kFinishLaunchBytes;
+    if (partial < kSegMinPartialBytes) return false;
+    return reread <= partial + (block > 512 ? 0 : kFinishLaunchBytes);
 }
 
 BwdPlan plan_bwd(const sp_desc_t* d) {
@@ -1247,19 +1321,28 @@ BwdPlan plan_bwd(const sp_desc_t* d) {
     };
     tile_rows(SP_BWD_TARGET_BLOCKS > 0 ? SP_BWD_TARGET_BLOCKS : kBwdVariants[p.variant].blocks);
     if (use_columns(R, H, elem_bytes(d->dtype), p.blocks, p.nacc, p.block)) {
+        // Rows split into equal segments of at most one batch each.
+        const int64_t most = col_segment_rows(p.block);
+        int64_t segs = (R + most - 1) / most;
+        if (segs < SP_COL_MIN_SEGS) segs = R < SP_COL_MIN_SEGS ? R : SP_COL_MIN_SEGS;
+        p.col_seg_rows = (R + segs - 1) / segs;
+        segs = (R + p.col_seg_rows - 1) / p.col_seg_rows;  // no empty segment
+        p.col_strips = (nchunk + kSeg - 1) / kSeg;
+        p.col_blocks = p.col_strips * segs;
+        if (segs > 1)
+            p.ws_bytes = kWsCountBytes + (size_t)segs * (size_t)p.nacc * (size_t)H * sizeof(float);
         // Column kernels are register-heavy (the 512-lane one fits one workgroup
         // per CU): size the row tiles so that row and column workgroups together
         // number one per CU, with all of a row workgroup's rows in flight where a
         // variant allows it.
-        p.col_blocks = (nchunk + kSeg - 1) / kSeg;
-        if (2 * p.col_blocks <= kColRowBlocks) {
+        if (2 * p.col_blocks <= col_row_blocks(p.block)) {
             if (SP_BWD_VARIANT < 0 && p.variant == kBwdCol512From) p.variant = kBwdCol512To;
-            tile_rows(kColRowBlocks - p.col_blocks);
+            tile_rows(col_row_blocks(p.block) - p.col_blocks);
         }
         return p;
     }
     const BwdVariant v = kBwdVariants[p.variant];
-    p.ws_bytes = (size_t)p.blocks * (size_t)p.nacc * (size_t)H * sizeof(float);
+    if (p.blocks > 0) p.ws_bytes = kWsCountBytes + (size_t)p.blocks * (size_t)p.nacc * (size_t)H * sizeof(float);
     p.lds_bytes = v.rg > 1 ? (size_t)v.rg * (size_t)p.nacc * (size_t)H * sizeof(float) : 0;
     return p;
 }
@@ -1310,6 +1393,13 @@ extern "C" int sp_region_traffic_bytes(const sp_desc_t* d, uint64_t* fwd_bytes, 
 extern "C" size_t sp_region_bwd_workspace_size(const sp_desc_t* d) {
     if (check_desc(d) != SP_OK) return 0;
     return plan_bwd(d).ws_bytes;
+}
+
+extern "C" int sp_region_bwd_schedule(const sp_desc_t* d) {
+    const int rc = check_desc(d);
+    if (rc != SP_OK) return rc;
+    const BwdPlan p = plan_bwd(d);
+    return p.col_blocks > 0 ? (int)(p.col_blocks / p.col_strips) : 0;
 }
 
 extern "C" int sp_region_fwd(const sp_desc_t* d, const void* const* P, const void* residual,
@@ -1450,10 +1540,13 @@ extern "C" int sp_region_bwd(const sp_desc_t* d, const void* dY, const void* h, 
     a.dR = dR;
     a.dres = d_residual;
     a.dP = dP;
-    a.ws = (float*)workspace;
+    a.col_count = plan.ws_bytes > 0 ? (uint32_t*)workspace : nullptr;
+    a.ws = plan.ws_bytes > 0 ? (float*)((char*)workspace + kWsCountBytes) : nullptr;
     a.dgamma = dgamma;
     a.dbeta = dbeta;
     a.col_blocks = (int32_t)plan.col_blocks;
+    a.col_strips = (int32_t)plan.col_strips;
+    a.col_seg_rows = plan.col_seg_rows;
     a.R = R;
     a.rows_per_block = plan.rows_per_block;
     a.H = (int32_t)H;
@@ -1482,7 +1575,7 @@ extern "C" int sp_region_bwd(const sp_desc_t* d, const void* dY, const void* h, 
     const int ncols = plan.nacc * (int)H;
     const unsigned fin_grid = (unsigned)((ncols / 4 + kFinGroups - 1) / kFinGroups);
     hipLaunchKernelGGL(sp_dgamma_finish_kernel, dim3(fin_grid), dim3(kFinGroups * kFinSlices), 0,
-                       (hipStream_t)stream, (const float*)workspace, plan.blocks, (int32_t)H,
+                       (hipStream_t)stream, (const float*)a.ws, plan.blocks, (int32_t)H,
                        (int32_t)plan.nacc, dgamma, dbeta);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? SP_OK : record_hip(e);
