@@ -73,6 +73,17 @@ def gdesc(w, j):
     return sp.make_desc(w.S, w.B, w.H, w.T, j, w.dtype, w.norm, w.eps, w.p, w.seed)
 
 
+# shards whose backward takes the partial-row and the 8-segment column dgamma schedules
+ROWS_SHARD = W.Workload("rows_T2_S16384_B1_H1024", 940, 2, 16384, 1, 1024, "bf16", "rms", 1e-6, 0.1, (1,))
+SEG8_SHARD = W.Workload("seg8_T2_S2048_B2_H2048", 942, 2, 2048, 2, 2048, "bf16", "rms", 1e-6, 0.1, (1,))
+
+
+def default_planner():
+    """False for a tuning build that forces one dgamma schedule on every shape."""
+    return (sp.sp_region_bwd_schedule(gdesc(ROWS_SHARD, 1)) == 0 and
+            sp.sp_region_bwd_schedule(gdesc(W.WORKLOADS["layernorm_T8_S4096_B1_H4096"], 3)) == 1)
+
+
 class Case:
     """Inputs of one workload: full tensors on the GPU, CPU copies on demand."""
 
@@ -312,19 +323,28 @@ def test_concurrent_calls_from_threads_and_streams():
                 assert torch.equal(b0[k], b[k]), (j, k)
 
 
-def test_runs_are_bitwise_identical():
-    w = W.WORKLOADS["layernorm_T8_S4096_B1_H4096"]
-    print(f"\n[case] {w.name}: two runs bitwise", flush=True)
+@pytest.mark.parametrize("w,j", [(W.WORKLOADS["layernorm_T8_S4096_B1_H4096"], 3), (SEG8_SHARD, 1),
+                                 (ROWS_SHARD, 1)], ids=lambda v: getattr(v, "name", str(v)))
+def test_runs_are_bitwise_identical(w, j):
+    """Two forwards, then eight backwards on one workspace, all bitwise equal
+    (one shard per dgamma schedule)."""
+    print(f"\n[case] {w.name}: repeated runs bitwise", flush=True)
     c = Case(w, "cuda")
-    a = gpu_fwd(c, 3)
-    ab = gpu_bwd(c, 3, a)
-    b = gpu_fwd(c, 3)
-    bb = gpu_bwd(c, 3, b)
+    a = gpu_fwd(c, j)
+    b = gpu_fwd(c, j)
     torch.cuda.synchronize()
-    for k in ("h", "y", "mask", "mean", "rstd"):
+    fk = ("h", "y", "mask", "rstd") + (("mean",) if w.norm == "ln" else ())
+    bk = ("d_res", "dP", "dgamma") + (("dbeta",) if w.norm == "ln" else ())
+    for k in fk:
         assert torch.equal(a[k], b[k]), k
-    for k in ("d_res", "dP", "dgamma", "dbeta"):
-        assert torch.equal(ab[k], bb[k]), k
+    d = gdesc(w, j)
+    ws = torch.zeros(max(16, sp.sp_region_bwd_workspace_size(d)), dtype=torch.uint8, device="cuda")
+    ref = sp.backward(d, c.shard(c.dY, j), a["h"], a["mask"], a["mean"], a["rstd"], c.gamma, workspace=ws)
+    for rep in range(8):
+        got = sp.backward(d, c.shard(c.dY, j), b["h"], b["mask"], b["mean"], b["rstd"], c.gamma, workspace=ws)
+        torch.cuda.synchronize()
+        for k in bk:
+            assert torch.equal(ref[k], got[k]), (rep, k)
 
 
 # ---------------------------------------------------------------------------
@@ -475,16 +495,6 @@ def test_gpu_argument_errors_leave_outputs_untouched():
     assert sp.sp_region_fwd(d, P, res, gam, None, h, h, m, None, rs) == -1
     torch.cuda.synchronize()
     assert bool((h == 3).all()) and bool((y == 3).all()) and bool((m == 3).all())
-
-
-ROWS_SHARD = W.Workload("rows_T2_S16384_B1_H1024", 940, 2, 16384, 1, 1024, "bf16", "rms", 1e-6, 0.1, (1,))
-SEG8_SHARD = W.Workload("seg8_T2_S2048_B2_H2048", 942, 2, 2048, 2, 2048, "bf16", "rms", 1e-6, 0.1, (1,))
-
-
-def default_planner():
-    """False for a tuning build that forces one dgamma schedule on every shape."""
-    return (sp.sp_region_bwd_schedule(gdesc(ROWS_SHARD, 1)) == 0 and
-            sp.sp_region_bwd_schedule(gdesc(W.WORKLOADS["layernorm_T8_S4096_B1_H4096"], 3)) == 1)
 
 
 @pytest.mark.parametrize("w,j,schedule", [(SEG8_SHARD, 1, 8),
