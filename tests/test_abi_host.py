@@ -260,7 +260,8 @@ def test_workspace_size_scales_with_norm(lib):
     ((2048, 2, 2048, 2, "bf16", "rms"), 8),    # 2048 rows of 2048: 8 segments of 256
     ((2056, 1, 2056, 2, "bf16", "ln"), 3),     # 1028 rows, a ragged last strip
     ((4100, 1, 1024, 2, "f32", "ln"), 9),      # 2050 fp32 rows: 9 segments of 228
-    ((1040, 1, 20480, 2, "bf16", "rms"), 0),   # 520 long rows: 1024-lane columns would spill
+    ((1040, 1, 20480, 2, "bf16", "rms"), 2),   # 520 long rows: 1024-lane rows always take columns
+    ((4096, 1, 16384, 2, "bf16", "ln"), 0),    # 2048 rows of 16384 (512 lanes x 4 chunks)
     ((1040, 1, 65536, 2, "bf16", "ln"), 2),    # 520 of the longest rows: partial rows too large
 ])
 def test_backward_schedule_by_shape(lib, shape, schedule):

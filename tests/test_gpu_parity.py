@@ -371,7 +371,7 @@ EDGE = [
     (4, 16, 2, 20480, "bf16", "ln", 0.1, 1),    # 2560-chunk rows: 1024 lanes x 4 chunks, in batches
     (3, 6, 1, 20480, "bf16", "rms", 0.2, 2),    # the same with a run-time T
     (2, 8, 1, 10240, "f32", "rms", 0.1, 0),     # fp32, 2560-chunk rows
-    (2, 1040, 1, 20480, "bf16", "rms", 0.1, 1), # 520 long rows, 1024 lanes x 4 chunks
+    (2, 1040, 1, 20480, "bf16", "rms", 0.1, 1), # 520 long rows, 1024 lanes x 4 chunks, 2 column segments
     (2, 1040, 1, 65536, "bf16", "ln", 0.1, 0),  # 520 of the longest rows, 8 chunks
     (8, 4080, 1, 4096, "bf16", "ln", 0.1, 2),   # 510 rows: column dgamma, ragged last 4-row tile
     (8, 4112, 1, 4096, "bf16", "ln", 0.1, 6),   # 514 rows: two column segments of 257 rows

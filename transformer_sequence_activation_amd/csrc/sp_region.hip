@@ -1036,12 +1036,13 @@ __global__ __launch_bounds__(RG* TPR) void sp_bwd_kernel(const BwdArgs a) {
 // order.  A block covers kFinGroups groups of four adjacent columns (one 16-byte
 // load each) and splits the G partial rows into kFinSlices contiguous slices, one
 // per lane; a lane issues all of its slice's loads before adding them in order,
-// then the slices are added in order through LDS.
+// then the slices are added pairwise through LDS (a fixed tree).
 #ifndef SP_FIN_SLICES
 #define SP_FIN_SLICES 32
 #endif
 constexpr int kFinGroups = 16;
 constexpr int kFinSlices = SP_FIN_SLICES;
+static_assert(kFinSlices > 0 && (kFinSlices & (kFinSlices - 1)) == 0, "the slice tree halves a power of two");
 constexpr int kFinBatch = 8;
 
 __global__ __launch_bounds__(kFinGroups* kFinSlices) void sp_dgamma_finish_kernel(
@@ -1070,12 +1071,14 @@ __global__ __launch_bounds__(kFinGroups* kFinSlices) void sp_dgamma_finish_kerne
     }
     part[sl][cg] = acc;
     __syncthreads();
-    if (sl == 0 && c < n) {
-        f32x4 s = part[0][cg];
 #pragma unroll
-        for (int q = 1; q < kFinSlices; ++q) s += part[q][cg];
+    for (int half = kFinSlices / 2; half >= 1; half /= 2) {
+        if (sl < half) part[sl][cg] += part[sl + half][cg];
+        __syncthreads();
+    }
+    if (sl == 0 && c < n) {
         float* dst = c < H ? dgamma + c : dbeta + (c - H);
-        *reinterpret_cast<f32x4*>(dst) = s;
+        *reinterpret_cast<f32x4*>(dst) = part[0][cg];
     }
 }
 
@@ -1291,15 +1294,15 @@ constexpr int64_t kSegMinPartialBytes = (int64_t)2 << 20;
 // partial rows (2 G nacc H 4 bytes written and read back) and no second launch.
 // Rows past one segment add the segments' arrival chain, which costs about as
 // much as the finish launch: several segments pay only where the partial rows
-// are large, and 1024-lane column workgroups (long rows, whose registers spill)
-// get no credit for the launch they save.
+// are large.  Rows of 1024-lane workgroups always take columns: there the
+// per-lane dgamma / dbeta accumulators of the partial-row schedule spill.
 bool use_columns(int64_t R, int64_t H, int eb, int64_t G, int nacc, int block) {
     if (SP_BWD_DG == 1 || R == 0) return false;
-    if (SP_BWD_DG == 2) return true;
+    if (SP_BWD_DG == 2 || block > 512) return true;
     const int64_t reread = 2 * R * H * eb, partial = 2 * G * nacc * H * 4;
     if (R <= col_segment_rows(block)) return reread <= partial + kFinishLaunchBytes;
     if (partial < kSegMinPartialBytes) return false;
-    return reread <= partial + (block > 512 ? 0 : kFinishLaunchBytes);
+    return reread <= partial + kFinishLaunchBytes;
 }
 
 BwdPlan plan_bwd(const sp_desc_t* d) {
