@@ -401,10 +401,12 @@ def test_edge_shapes_match_oracle(T, S, B, H, dtype, norm, p, j):
         assert bool(g["mask"].all())
 
 
-@pytest.mark.parametrize("norm,H", [("rms", 1024), ("ln", 1024), ("ln", 4096)])
-def test_residual_gradient_input(norm, H):
-    print(f"\n[case] dR input, {norm}, H={H}", flush=True)
-    c = _edge_case(4, 64, 2, H, "bf16", norm, 0.2, 1)
+@pytest.mark.parametrize("norm,H,S,B", [("rms", 1024, 64, 2), ("ln", 1024, 64, 2), ("ln", 4096, 64, 2),
+                                        ("ln", 2048, 2048, 2), ("rms", 1024, 32768, 1)])
+def test_residual_gradient_input(norm, H, S, B):
+    """The last two shards take the 4-segment column and the partial-row dgamma schedules."""
+    print(f"\n[case] dR input, {norm}, S={S} B={B} H={H}", flush=True)
+    c = _edge_case(4, S, B, H, "bf16", norm, 0.2, 1)
     j = 1
     dR_full = W._randn((c.w.S, c.w.B, c.w.H), 1.0, "cpu", 4242).to(torch.bfloat16)
     dR = c.shard(dR_full, j).cuda()
@@ -569,13 +571,15 @@ def test_workspace_reused_across_calls_and_shapes():
     assert not bool(counts.any())  # every call left its arrival counts at zero
 
 
-@pytest.mark.parametrize("name,j", [("layernorm_T8_S4096_B1_H4096", 3), ("minimind_T2_S2048_B2_H768", 1)])
-def test_recomputed_mask_matches_stored_mask(name, j):
+@pytest.mark.parametrize("w,j", [(W.WORKLOADS["layernorm_T8_S4096_B1_H4096"], 3),
+                                 (W.WORKLOADS["minimind_T2_S2048_B2_H768"], 1), (SEG8_SHARD, 1)],
+                         ids=lambda v: getattr(v, "name", str(v)))
+def test_recomputed_mask_matches_stored_mask(w, j):
     """With SP_FLAG_RECOMPUTE_MASK the forward keeps no mask and the backward
     regenerates the flags: every output is bit-identical to the stored-mask run,
-    and the backward matches the oracle (which uses its own stored mask)."""
-    print(f"\n[case] {name} shard {j}: recomputed mask", flush=True)
-    w = W.WORKLOADS[name]
+    and the backward matches the oracle (which uses its own stored mask).  One
+    shard per dgamma schedule."""
+    print(f"\n[case] {w.name} shard {j}: recomputed mask", flush=True)
     c = Case(w, "cpu")
     f = gpu_fwd(c, j)
     b = gpu_bwd(c, j, f)
