@@ -401,6 +401,51 @@ def test_edge_shapes_match_oracle(T, S, B, H, dtype, norm, p, j):
         assert bool(g["mask"].all())
 
 
+def _random_shapes(n, seed, rows, max_elems=1 << 22):
+    """Seeded shard shapes spread over the launch layouts and dgamma schedules:
+    T, row length and token rows (log-uniform), dtype, norm, p and j drawn at
+    random."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        dtype = "f32" if rng.random() < 0.25 else "bf16"
+        per = 4 if dtype == "f32" else 8  # elements per 16 bytes
+        max_chunks = (1 << 15) // per if dtype == "f32" else (1 << 16) // per
+        H = per * int(np.exp(rng.uniform(0.0, np.log(max_chunks))))
+        T = int(rng.choice([1, 2, 3, 4, 8]))
+        B = int(rng.choice([1, 2, 3]))
+        R = int(np.exp(rng.uniform(np.log(rows[0]), np.log(rows[1]))))
+        S = T * max(1, -(-R // B))
+        if (S // T) * B * H > max_elems:
+            continue
+        out.append((T, S, B, H, dtype, str(rng.choice(["rms", "ln"])), float(rng.choice([0.0, 0.1, 0.5])),
+                    int(rng.integers(0, T))))
+    return out
+
+
+# short shards of any length, then long ones (the segmented and partial-row schedules)
+RANDOM = _random_shapes(8, 2024, (1, 600)) + _random_shapes(8, 2025, (600, 8192))
+
+
+def test_random_shapes_cover_every_schedule():
+    scheds = {min(sp.sp_region_bwd_schedule(sp.make_desc(S, B, H, T, j, dt, n)), 2)
+              for T, S, B, H, dt, n, p, j in RANDOM}
+    if default_planner():
+        assert scheds == {0, 1, 2}, scheds
+
+
+@pytest.mark.parametrize("T,S,B,H,dtype,norm,p,j", RANDOM)
+def test_random_shapes_match_oracle(T, S, B, H, dtype, norm, p, j):
+    print(f"\n[case] random T={T} S={S} B={B} H={H} {dtype} {norm} p={p} j={j}", flush=True)
+    c = _edge_case(T, S, B, H, dtype, norm, p, j, seed=7)
+    g = gpu_fwd(c, j)
+    gb = gpu_bwd(c, j, g)
+    torch.cuda.synchronize()
+    o = oracle_fwd(c, j)
+    compare_fwd(c.w, g, o)
+    compare_bwd(c.w, gb, oracle_bwd(c, j, o))
+
+
 @pytest.mark.parametrize("norm,H,S,B", [("rms", 1024, 64, 2), ("ln", 1024, 64, 2), ("ln", 4096, 64, 2),
                                         ("ln", 2048, 2048, 2), ("rms", 1024, 32768, 1)])
 def test_residual_gradient_input(norm, H, S, B):
