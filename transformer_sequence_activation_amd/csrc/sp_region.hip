@@ -1086,20 +1086,30 @@ __global__ __launch_bounds__(kFinGroups* kFinSlices) void sp_dgamma_finish_kerne
 // Launch layouts: (lanes per row, chunks per lane) by row length in chunks.
 
 struct Layout {
-    int tpr, cpt;
+    int tpr, cpt, limit;  // the default choice for rows of up to `limit` chunks
 };
-// In increasing capacity (tpr * cpt chunks); the first that holds the row is
-// used.  X(lanes per row, chunks per lane, ...): the host table and the kernel
-// tables below are both generated from this list.
-#define SP_LAYOUT_LIST(X, ...)                                                                    \
-    X(16, 1, __VA_ARGS__), X(32, 1, __VA_ARGS__), X(64, 1, __VA_ARGS__), X(32, 3, __VA_ARGS__),   \
-        X(64, 2, __VA_ARGS__), X(64, 3, __VA_ARGS__), X(64, 4, __VA_ARGS__),                      \
-        X(512, 1, __VA_ARGS__), X(512, 2, __VA_ARGS__), X(512, 4, __VA_ARGS__),                   \
-        X(1024, 4, __VA_ARGS__), X(1024, 8, __VA_ARGS__)
-#define SP_LAYOUT_STRUCT(TPR, CPT, ...) Layout{TPR, CPT}
+// X(lanes per row, chunks per lane, longest row it is chosen for, ...), in
+// increasing limit: the first whose limit holds the row is used.  One chunk per
+// lane wherever a row fills most of a power-of-two lane group (more wavefronts
+// per SIMD to hide the arithmetic); rows of 113-128 chunks measured faster at
+// two chunks per lane.  The host table and the kernel tables below are both
+// generated from this list.
+#define SP_LAYOUT_LIST(X, ...)                                                                  \
+    X(16, 1, 16, __VA_ARGS__), X(32, 1, 32, __VA_ARGS__), X(64, 1, 64, __VA_ARGS__),            \
+        X(128, 1, 112, __VA_ARGS__), X(64, 2, 128, __VA_ARGS__), X(256, 1, 256, __VA_ARGS__),   \
+        X(512, 1, 512, __VA_ARGS__), X(512, 2, 1024, __VA_ARGS__), X(512, 4, 2048, __VA_ARGS__), \
+        X(1024, 4, 4096, __VA_ARGS__), X(1024, 8, 8192, __VA_ARGS__)
+#define SP_LAYOUT_STRUCT(TPR, CPT, LIMIT, ...) Layout{TPR, CPT, LIMIT}
 constexpr Layout kLayouts[] = {SP_LAYOUT_LIST(SP_LAYOUT_STRUCT, 0)};
 constexpr int kNumLayouts = sizeof(kLayouts) / sizeof(kLayouts[0]);
-constexpr int kNumDefault = kNumLayouts;
+constexpr bool layouts_ok() {
+    for (int i = 0; i < kNumLayouts; ++i) {
+        if (kLayouts[i].tpr * kLayouts[i].cpt < kLayouts[i].limit) return false;
+        if (i > 0 && kLayouts[i].limit <= kLayouts[i - 1].limit) return false;
+    }
+    return kLayouts[kNumLayouts - 1].limit == SP_MAX_H_BYTES / 16;
+}
+static_assert(layouts_ok(), "each layout holds its rows; limits increase up to the longest row");
 #ifndef SP_SUBWAVE_BLOCK
 #define SP_SUBWAVE_BLOCK 256
 #endif
@@ -1154,7 +1164,7 @@ constexpr int64_t col_row_blocks(int block) { return block <= 256 ? SP_COL_ROW_B
 typedef void (*FwdKernel)(FwdArgs);
 typedef void (*BwdKernel)(BwdArgs);
 
-#define SP_FWD_ENTRY(TPR, CPT, DT, TT) &sp_fwd_kernel<DT, TT, TPR, CPT, block_of(TPR)>
+#define SP_FWD_ENTRY(TPR, CPT, LIMIT, DT, TT) &sp_fwd_kernel<DT, TT, TPR, CPT, block_of(TPR)>
 #define SP_BWD_ENTRY(TPR, CPT, RG, PF, BLOCKS, DT, NORM, HDR, REGEN, COLS) \
     &sp_bwd_kernel<DT, NORM, TPR, CPT, RG, PF, HDR, REGEN, COLS>
 
@@ -1232,8 +1242,8 @@ int capacity(int li) { return kLayouts[li].tpr * kLayouts[li].cpt; }
 
 int pick_layout(int64_t nchunk, int forced) {
     if (forced >= 0 && forced < kNumLayouts && nchunk <= capacity(forced)) return forced;
-    for (int i = 0; i < kNumDefault; ++i)
-        if (nchunk <= capacity(i)) return i;
+    for (int i = 0; i < kNumLayouts; ++i)
+        if (nchunk <= kLayouts[i].limit) return i;
     return -1;
 }
 
