@@ -1040,7 +1040,10 @@ __global__ __launch_bounds__(RG* TPR) void sp_bwd_kernel(const BwdArgs a) {
 #ifndef SP_FIN_SLICES
 #define SP_FIN_SLICES 32
 #endif
-constexpr int kFinGroups = 16;
+#ifndef SP_FIN_GROUPS
+#define SP_FIN_GROUPS 8
+#endif
+constexpr int kFinGroups = SP_FIN_GROUPS;
 constexpr int kFinSlices = SP_FIN_SLICES;
 static_assert(kFinSlices > 0 && (kFinSlices & (kFinSlices - 1)) == 0, "the slice tree halves a power of two");
 constexpr int kFinBatch = 8;
