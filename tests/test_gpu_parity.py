@@ -272,12 +272,13 @@ def test_long_sequence_all_shards():
     assert abs(keep_total - Nt * (1 - w.p)) <= 5 * math.sqrt(Nt * w.p * (1 - w.p))
 
 
-def test_concurrent_calls_from_threads_and_streams():
+@pytest.mark.parametrize("w", [W.WORKLOADS["minimind_T2_S2048_B2_H768"], SEG8_SHARD], ids=lambda v: v.name)
+def test_concurrent_calls_from_threads_and_streams(w):
     """The library holds no state: two host threads, each with its own stream,
     workspace and shard, enqueue forward + backward at the same time; every
-    output equals the sequential run bit for bit."""
+    output equals the sequential run bit for bit (partial-row and segmented
+    column dgamma schedules)."""
     import threading
-    w = W.WORKLOADS["minimind_T2_S2048_B2_H768"]
     print(f"\n[case] {w.name}: shards 0 and 1 from two threads on two streams", flush=True)
     c = Case(w, "cuda")
     ref = {}
