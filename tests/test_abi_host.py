@@ -9,6 +9,8 @@ import ctypes
 import os
 import re
 
+import numpy as np
+
 import pytest
 
 import transformer_sequence_activation_amd as sp
@@ -283,3 +285,34 @@ def test_schedule_of_a_bad_descriptor(lib):
     assert lib.sp_region_bwd_schedule(None) == -1
     assert sp.sp_region_bwd_schedule(good_desc(S=66)) == -2
     assert sp.sp_region_bwd_schedule(good_desc(S=0)) == 0
+
+
+def test_schedule_and_workspace_agree_on_random_shapes(lib):
+    """Host planner invariants over seeded random descriptors: a single column
+    segment needs no workspace; k >= 2 segments need the 4096 count bytes plus k
+    segment sums; partial rows need the count bytes plus whole partial rows."""
+    rng = np.random.default_rng(77)
+    seen = set()
+    for _ in range(400):
+        dtype = "f32" if rng.random() < 0.3 else "bf16"
+        per = 4 if dtype == "f32" else 8
+        H = per * int(np.exp(rng.uniform(0.0, np.log(65536 // per if dtype == "bf16" else 32768 // per))))
+        T = int(rng.choice([1, 2, 4, 8, 16]))
+        B = int(rng.integers(1, 5))
+        S = T * int(np.exp(rng.uniform(0.0, np.log(20000))))
+        norm = str(rng.choice(["rms", "ln"]))
+        d = sp.make_desc(S, B, H, T, int(rng.integers(0, T)), dtype, norm)
+        k = sp.sp_region_bwd_schedule(d)
+        ws = sp.sp_region_bwd_workspace_size(d)
+        nacc = 2 if norm == "ln" else 1
+        assert k >= 0
+        if k == 1:
+            assert ws == 0
+        elif k >= 2:
+            assert ws == 4096 + k * nacc * H * 4
+            assert k <= d.R  # no empty segment
+        else:
+            assert ws > 4096 and (ws - 4096) % (nacc * H * 4) == 0
+            assert (ws - 4096) // (nacc * H * 4) <= d.R  # no more partial rows than token rows
+        seen.add(min(k, 2))
+    assert seen == {0, 1, 2}
