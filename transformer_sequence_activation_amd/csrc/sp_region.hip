@@ -1039,7 +1039,8 @@ __global__ __launch_bounds__(RG* TPR) void sp_bwd_kernel(const BwdArgs a) {
 // order.  A block covers kFinGroups groups of four adjacent columns (one 16-byte
 // load each) and splits the G partial rows into kFinSlices contiguous slices, one
 // per lane; a lane issues all of its slice's loads before adding them in order,
-// then the slices are added pairwise through LDS (a fixed tree).
+// then the slices are added in a fixed tree (lane butterfly inside a wavefront,
+// the wavefronts in order through LDS).
 #ifndef SP_FIN_SLICES
 #define SP_FIN_SLICES 32
 #endif
@@ -1048,12 +1049,14 @@ __global__ __launch_bounds__(RG* TPR) void sp_bwd_kernel(const BwdArgs a) {
 #endif
 constexpr int kFinGroups = SP_FIN_GROUPS;
 constexpr int kFinSlices = SP_FIN_SLICES;
-static_assert(kFinSlices > 0 && (kFinSlices & (kFinSlices - 1)) == 0, "the slice tree halves a power of two");
+static_assert(kWave % kFinGroups == 0 && (kFinGroups * kFinSlices) % kWave == 0,
+              "a wavefront holds whole slices of every column group");
 constexpr int kFinBatch = 8;
 
 __global__ __launch_bounds__(kFinGroups* kFinSlices) void sp_dgamma_finish_kernel(
     const float* ws, int64_t G, int32_t H, int32_t nacc, float* dgamma, float* dbeta) {
-    __shared__ f32x4 part[kFinSlices][kFinGroups];
+    constexpr int NW = kFinGroups * kFinSlices / kWave;
+    __shared__ f32x4 part[NW][kFinGroups];
     const int n = nacc * H;  // a multiple of 4
     const int cg = threadIdx.x % kFinGroups;
     const int sl = threadIdx.x / kFinGroups;
@@ -1075,16 +1078,21 @@ __global__ __launch_bounds__(kFinGroups* kFinSlices) void sp_dgamma_finish_kerne
         }
         for (; g < g1; ++g) acc += *reinterpret_cast<const f32x4*>(src + g * n);
     }
-    part[sl][cg] = acc;
-    __syncthreads();
+    // the slices of one wavefront by a lane butterfly, then the wavefronts in order
 #pragma unroll
-    for (int half = kFinSlices / 2; half >= 1; half /= 2) {
-        if (sl < half) part[sl][cg] += part[sl + half][cg];
-        __syncthreads();
+    for (int m = kFinGroups; m < kWave; m *= 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], m);
     }
-    if (sl == 0 && c < n) {
+    const int w = threadIdx.x / kWave;
+    if (threadIdx.x % kWave < kFinGroups) part[w][cg] = acc;
+    __syncthreads();
+    if (threadIdx.x < kFinGroups && c < n) {
+        f32x4 t = part[0][cg];
+#pragma unroll
+        for (int q = 1; q < NW; ++q) t += part[q][cg];
         float* dst = c < H ? dgamma + c : dbeta + (c - H);
-        *reinterpret_cast<f32x4*>(dst) = part[0][cg];
+        *reinterpret_cast<f32x4*>(dst) = t;
     }
 }
 
