@@ -487,6 +487,22 @@ def test_rounding_ties_to_even():
     assert np.all((exact & 0xFFFF) == 0x8000)
 
 
+@pytest.mark.parametrize("norm", ["ln", "rms"])
+def test_large_offset_rows(norm):
+    """Rows whose mean is a thousand times their spread (a residual stream offset
+    by 1000): the statistics are fp32 two-pass sums over the rounded h, so the
+    variance keeps its digits and y still matches the oracle."""
+    print(f"\n[case] residual offset by 1000, {norm}", flush=True)
+    c = _edge_case(4, 256, 2, 4096, "bf16", norm, 0.1, 2)
+    c.res += 1000.0
+    g = gpu_fwd(c, 2)
+    gb = gpu_bwd(c, 2, g)
+    torch.cuda.synchronize()
+    o = oracle_fwd(c, 2)
+    compare_fwd(c.w, g, o)
+    compare_bwd(c.w, gb, oracle_bwd(c, 2, o))
+
+
 def test_nonfinite_input_stays_in_its_row():
     """An infinite partial element (kept by dropout) makes only its own token row
     non-finite; every other row of the shard still matches the oracle."""
