@@ -466,6 +466,8 @@ def main():
     import transformer_sequence_activation_amd as sp
     from transformer_sequence_activation_amd import workloads as W
 
+    import __graft_entry__
+    __graft_entry__.build_if_missing()
     sp.load()
     torch.cuda.set_device(0)
     stream = torch.cuda.Stream()

@@ -12,6 +12,13 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
 
 
+def pytest_sessionstart(session):
+    # a fresh checkout has no built library yet: build it (hipcc cross-compiles
+    # for gfx950 without a GPU); a built one is used as it is
+    import __graft_entry__
+    __graft_entry__.build_if_missing()
+
+
 def gpu_available():
     try:
         import torch
