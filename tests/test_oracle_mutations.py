@@ -35,6 +35,11 @@ MUTATIONS = [
      "for (t = 1; t < d->T - 1; ++t) acc = acc + (float)load_elem(P[t], i, d->dtype);"),
     ("bf16 by truncation instead of round-to-nearest-even",
      "u += 0x7FFFu + ((u >> 16) & 1u);", "u += 0u;"),
+    ("fp32-mode partials summed in double",
+     "float acc = (float)load_elem(P[0], i, d->dtype);", "double acc = (double)load_elem(P[0], i, d->dtype);"),
+    ("fp32-mode backward scaled by the double 1/(1-p)",
+     "if (d->dtype != SPO_F64) scale = (double)(float)scale;",
+     "if (d->dtype == SPO_BF16) scale = (double)(float)scale;"),
     ("LayerNorm bias added with the wrong sign",
      "gamma[k] * ((hrow[k] - mu) * rs) + beta[k]", "gamma[k] * ((hrow[k] - mu) * rs) - beta[k]"),
 ]

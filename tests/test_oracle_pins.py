@@ -329,6 +329,88 @@ def test_bf16_forward_matches_exact_mode_to_one_rounding(norm):
     assert np.all(np.abs(y16 - o64["y"]) <= 2 * ulp * scale)
 
 
+# ---------------------------------------------------------------------------
+# The fp32 activation mode (the tiny fp32 workload runs on it).
+
+@pytest.mark.parametrize("T,p,norm", [(1, 0.0, oracle.RMSNORM), (3, 0.1, oracle.LAYERNORM),
+                                      (8, 0.1, oracle.RMSNORM), (2, 0.5, oracle.LAYERNORM)])
+def test_f32_forward_h_matches_torch_float32_chain(T, p, norm):
+    """In the fp32 mode h is the fp32 chain P_0 + P_1 + ... (t ascending), times
+    the fp32 value of 1/(1-p) where kept, plus the residual: torch's float32
+    element-wise ops on the same values give the same bits."""
+    S, B, H, j = 8 * T, 2, 72, T - 1
+    rng = np.random.default_rng(60 + T)
+    P = [(rng.standard_normal((S, B, H)) / math.sqrt(T)).astype(np.float32) for _ in range(T)]
+    res = rng.standard_normal((S, B, H)).astype(np.float32)
+    gam = 1 + 0.02 * rng.standard_normal(H)
+    bet = 0.02 * rng.standard_normal(H) if norm == oracle.LAYERNORM else None
+    d = desc(S, B, H, T, j, oracle.F32, norm, 1e-5, p)
+    Ps = [shard_rows(x, S, B, H, T, j) for x in P]
+    rs = shard_rows(res, S, B, H, T, j)
+    out = oracle.fwd(d, Ps, rs, gam, bet)
+    R = (S // T) * B
+    mask = oracle.keep_mask(1234, p, j * R * H, R * H).reshape(R, H).astype(bool)
+    assert np.array_equal(out["mask"].astype(bool), mask)
+    acc = torch.from_numpy(Ps[0].copy())
+    for x in Ps[1:]:
+        acc = acc + torch.from_numpy(x)
+    scale32 = torch.tensor(float(np.float32(1.0 / (1.0 - float(np.float32(p))))), dtype=torch.float32)
+    z = torch.where(torch.from_numpy(mask), acc * scale32, torch.zeros((), dtype=torch.float32))
+    h = torch.from_numpy(rs) + z
+    assert h.dtype == torch.float32
+    assert np.array_equal(out["h"].view(np.uint32), h.numpy().view(np.uint32))
+
+
+@pytest.mark.parametrize("norm", [oracle.RMSNORM, oracle.LAYERNORM])
+def test_f32_forward_norm_is_exact_mode_rounded_once(norm):
+    """The fp32 mode's statistics are those of its stored h, and y is the exact
+    mode's y of that h rounded once to fp32 (the exact mode fed h as its single
+    partial, with p = 0 and a zero residual, reproduces h without rounding)."""
+    S, B, H, T, j = 16, 2, 96, 4, 1
+    P, res, gam, bet = _f64_case(S, B, H, T, j, 61)
+    bet = bet if norm == oracle.LAYERNORM else None
+    P32 = [x.astype(np.float32) for x in P]
+    d32 = desc(S, B, H, T, j, oracle.F32, norm, 1e-6, 0.1)
+    o32 = oracle.fwd(d32, [shard_rows(x, S, B, H, T, j) for x in P32],
+                     shard_rows(res.astype(np.float32), S, B, H, T, j), gam, bet)
+    R = (S // T) * B
+    d64 = desc(S // T, B, H, 1, 0, oracle.F64, norm, 1e-6, 0.0)
+    o64 = oracle.fwd(d64, [o32["h"].astype(np.float64)], np.zeros((R, H)), gam, bet)
+    assert np.array_equal(o64["h"], o32["h"].astype(np.float64))
+    assert np.array_equal(o32["rstd"], o64["rstd"])
+    if norm == oracle.LAYERNORM:
+        assert np.array_equal(o32["mean"], o64["mean"])
+    assert np.array_equal(o32["y"].view(np.uint32), o64["y"].astype(np.float32).view(np.uint32))
+
+
+@pytest.mark.parametrize("norm,p", [(oracle.RMSNORM, 0.1), (oracle.LAYERNORM, 0.3)])
+def test_f32_backward_is_exact_mode_rounded_once(norm, p):
+    """The fp32 mode's backward on fp32 inputs: d_res is the exact mode's d_res
+    rounded once; dP is that unrounded gradient times the fp32 value of
+    1/(1-p), rounded once; dgamma / dbeta are the exact mode's sums."""
+    S, B, H, T, j = 16, 2, 80, 2, 1
+    rng = np.random.default_rng(62)
+    R = (S // T) * B
+    h = rng.standard_normal((R, H)).astype(np.float32)
+    dY = rng.standard_normal((R, H)).astype(np.float32)
+    mask = oracle.keep_mask(1234, p, j * R * H, R * H).reshape(R, H)
+    hf = h.astype(np.float64)
+    mean = hf.mean(axis=1).astype(np.float32).astype(np.float64) if norm == oracle.LAYERNORM else None
+    cen = hf - (mean[:, None] if mean is not None else 0)
+    rstd = (1 / np.sqrt((cen ** 2).mean(axis=1) + 1e-6)).astype(np.float32).astype(np.float64)
+    gam = 1 + 0.02 * rng.standard_normal(H)
+    g32 = oracle.bwd(desc(S, B, H, T, j, oracle.F32, norm, 1e-6, p), dY, h, mask, mean, rstd, gam)
+    g64 = oracle.bwd(desc(S, B, H, T, j, oracle.F64, norm, 1e-6, p), dY.astype(np.float64), hf, mask,
+                     mean, rstd, gam)
+    assert np.array_equal(g32["d_res"].view(np.uint32), g64["d_res"].astype(np.float32).view(np.uint32))
+    scale32 = np.float64(np.float32(1.0 / (1.0 - float(np.float32(p)))))
+    want_dP = np.where(mask == 1, g64["d_res"] * scale32, 0.0).astype(np.float32)
+    assert np.array_equal(g32["dP"].view(np.uint32), want_dP.view(np.uint32))
+    assert np.array_equal(g32["dgamma"], g64["dgamma"])
+    if norm == oracle.LAYERNORM:
+        assert np.array_equal(g32["dbeta"], g64["dbeta"])
+
+
 def test_dropout_scale_is_inverted_like_torch():
     """Kept elements carry x/(1-p) exactly as torch's dropout; the mean is kept."""
     S, B, H, p = 64, 4, 512, 0.25
