@@ -2,7 +2,7 @@
 kernel trace, and rocprofv3's own --stats summary) and, when the run collected
 them, the FETCH_SIZE / WRITE_SIZE hardware counters.
 
-    python -m transformer_sequence_activation_amd.rocprof_summary RESULTS.db [...]
+    python -m measure.rocprof_summary RESULTS.db [...]
         [--copy-bytes N] [--filter SUBSTRING]
 
 FETCH_SIZE and WRITE_SIZE are reported by the profiler in KiB per dispatch.

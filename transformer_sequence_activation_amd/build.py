@@ -3,6 +3,10 @@
     python -m transformer_sequence_activation_amd.build [--resource-usage] [-D NAME=VALUE ...]
     python -m transformer_sequence_activation_amd.build --resource-table 'sp_fwd_kernel<1, 8, 512, 1, 512>;...'
 
+The device code is compiled in a pass of its own, with packed fp32 instructions
+(v_pk_add/mul/fma_f32) switched off; the host pass then embeds that code
+object.  The feature exists only for the GPU target, so giving it to the host
+pass as well would make the host compiler warn about an unknown feature.
 """
 import argparse
 import os
@@ -13,51 +17,57 @@ ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "sp_region.hip")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsp_region.so")
-PROBE_SRC = os.path.join(PKG, "csrc", "stream_probe.hip")
-PROBE = os.path.join(PKG, "stream_probe")
 ARCH = "gfx950"
 
-HIPCC_FLAGS = [
-    f"--offload-arch={ARCH}",
-    "-O3",
-    "-std=c++17",
-    "-fPIC",
-    "-shared",
-    # no packed fp32 instructions (v_pk_add/mul/fma_f32) anywhere in the device code
-    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-]
+COMMON = [f"--offload-arch={ARCH}", "-O3", "-std=c++17"]
+# no packed fp32 instructions anywhere in the device code
+DEVICE_ONLY = ["--cuda-device-only", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def _hipcc():
+    return os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
+
+
+def _run(cmd, verbose, capture=False):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    return subprocess.run(cmd, check=True, capture_output=capture, text=capture)
 
 
 def build(out=LIB, defines=(), resource_usage=False, verbose=False):
-    """Compile csrc/sp_region.hip into `out`; always recompiles.  Returns the path."""
-    hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", INCLUDE]
-    cmd += [f"-D{d}" for d in defines]
-    if resource_usage:
-        cmd += ["-Rpass-analysis=kernel-resource-usage"]
+    """Compile csrc/sp_region.hip into `out`; always recompiles.  Returns the path.
+
+    With resource_usage=True the compiler's kernel-resource remarks of the
+    device pass are returned instead (the library is still built)."""
+    defs = [f"-D{d}" for d in defines]
+    fatbin = out + ".hipfb.tmp"
     tmp = out + ".tmp"
-    cmd += [SRC, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, out)
-    return out
+    dev = [_hipcc(), *COMMON, *DEVICE_ONLY, "-I", INCLUDE, *defs]
+    if resource_usage:
+        dev += ["-Rpass-analysis=kernel-resource-usage"]
+    try:
+        r = _run(dev + [SRC, "-o", fatbin], verbose, capture=resource_usage)
+        host = [_hipcc(), *COMMON, "--cuda-host-only", "-fPIC", "-shared", "-I", INCLUDE, *defs,
+                "-Xclang", "-fcuda-include-gpubinary", "-Xclang", fatbin, SRC, "-o", tmp]
+        _run(host, verbose)
+        os.replace(tmp, out)
+    finally:
+        for f in (fatbin, tmp):
+            if os.path.exists(f):
+                os.remove(f)
+    return r.stderr if resource_usage else out
 
 
 def resource_table(out, kernels=None):
     """Build `out` with the compiler's kernel-resource remarks and return a text
     table (kernel, VGPRs, AGPRs, SGPRs, spills, scratch, LDS, waves per SIMD),
     keeping kernels whose demangled name contains one of `kernels`."""
-    hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
-    tmp = out + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", INCLUDE, "-Rpass-analysis=kernel-resource-usage", SRC, "-o", tmp]
-    r = subprocess.run(cmd, check=True, capture_output=True, text=True)
-    os.replace(tmp, out)
+    stderr = build(out, resource_usage=True)
     rows, cur = [], None
     keys = {"VGPRs": "vgpr", "AGPRs": "agpr", "TotalSGPRs": "sgpr", "VGPRs Spill": "vspill",
             "ScratchSize [bytes/lane]": "scratch", "LDS Size [bytes/block]": "lds",
             "Occupancy [waves/SIMD]": "occ"}
-    for line in r.stderr.splitlines():
+    for line in stderr.splitlines():
         if "remark:" not in line:
             continue
         body = line.split("remark:", 1)[1].split("[-Rpass", 1)[0].strip()
@@ -82,25 +92,10 @@ def resource_table(out, kernels=None):
     return "\n".join(out_lines)
 
 
-def build_probe(out=PROBE, verbose=False):
-    """Compile the streaming-bandwidth probe executable; always recompiles."""
-    hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
-    flags = [f for f in HIPCC_FLAGS if f not in ("-fPIC", "-shared")]
-    tmp = out + ".tmp"
-    cmd = [hipcc, *flags, PROBE_SRC, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, out)
-    return out
-
-
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--out", default=LIB)
     ap.add_argument("-D", dest="defines", action="append", default=[])
-    ap.add_argument("--resource-usage", action="store_true")
-    ap.add_argument("--probe", action="store_true", help="also build the stream_probe executable")
     ap.add_argument("--resource-table", metavar="KERNELS", default=None,
                     help="build and print the resource table of the kernels whose names contain one "
                          "of these ';'-separated substrings ('' = all)")
@@ -108,6 +103,4 @@ if __name__ == "__main__":
     if args.resource_table is not None:
         print(resource_table(args.out, [k for k in args.resource_table.split(";") if k]))
         raise SystemExit(0)
-    print(build(args.out, args.defines, args.resource_usage, verbose=True))
-    if args.probe:
-        print(build_probe(verbose=True))
+    print(build(args.out, args.defines, verbose=True))
