@@ -36,8 +36,9 @@
  *              reaches that point.
  *   Errors     Argument errors are returned synchronously, before anything is
  *              enqueued.  A failed launch returns SP_EHIP (the text is kept for
- *              sp_region_strerror).  Calls are thread-safe; the library holds
- *              no state.
+ *              sp_region_strerror).  Calls are thread-safe and the library
+ *              keeps no state of its own; the backward's workspace carries
+ *              arrival counts from call to call (see sp_region_bwd).
  *   Empty      S == 0 or B == 0 is an empty shard: the forward enqueues
  *              nothing, the backward writes zeros to dgamma/dbeta.
  */
@@ -122,18 +123,26 @@ int sp_region_fwd(const sp_desc_t* d, const void* const* P, const void* residual
                   float* mean_out, float* rstd_out, void* stream);
 
 /*
- * Backward of the SP region on shard j (the derivative of the forward above;
- * the dropout backward multiplies by the saved mask, and because the forward
- * sums the partials, every P_t receives the same gradient dP).
+ * Backward of the SP region on shard j: the derivative of the forward above.
+ *
+ *   "Sequence Parallel" (formulaic.cloudchewie.com), section "MLP activation
+ *   size": the backward of dropout multiplies the incoming gradient by the
+ *   saved 0/1 mask (here with the forward's 1/(1-p) scale, inverted dropout).
+ *   "MiniMind-tron: Sequence Parallelism", section 3.3.3.1: the forward sums
+ *   the partials, and the backward of a sum hands every addend the same
+ *   gradient, so one dP serves all T partials P_t.  Section 3.4.2.1: the norm
+ *   weights are replicated while each rank sees only its S/T tokens, so the
+ *   dgamma / dbeta of one shard are partial sums that still have to be summed
+ *   over the T ranks (outside this call).
+ *   The norm derivatives themselves are not printed on the pages; they are the
+ *   standard ones of the forward's formulas:
  *
  *   xhat = (h - mean) * rstd  (mean = 0 for RMSNorm),  g = dY * gamma
  *   RMSNorm  : dh = rstd * (g - xhat * mean_k(g * xhat))
  *   LayerNorm: dh = rstd * (g - mean_k(g) - xhat * mean_k(g * xhat))
  *   dh += dR (when given)
  *   d_residual = round(dh);  dP = round(keep ? dh * (1/(1-p)) : +0)
- *   dgamma[k] = sum_r dY * xhat;  dbeta[k] = sum_r dY   (this shard's rows only:
- *   the norm weights are replicated, so the partials of all shards still have to
- *   be summed across ranks)
+ *   dgamma[k] = sum_r dY * xhat;  dbeta[k] = sum_r dY   (this shard's rows only)
  *
  * dY        shard gradient of y.  h, mask (NULL with SP_FLAG_RECOMPUTE_MASK), mean
  *           (LayerNorm; NULL for RMSNorm), rstd: as saved by sp_region_fwd.
@@ -144,19 +153,27 @@ int sp_region_fwd(const sp_desc_t* d, const void* const* P, const void* residual
  * dgamma    [H] fp32, overwritten.  dbeta: [H] fp32 for LayerNorm, NULL for RMSNorm.
  * workspace device scratch of at least sp_region_bwd_workspace_size(d) bytes,
  *           16-byte aligned, zero-filled before the first call that uses it.
- *           Its first 4096 bytes hold arrival counts that every call leaves at
- *           zero again; the rest is scratch.  So one zero fill at allocation
- *           serves every later call, for any descriptor, as long as only
- *           sp_region_bwd writes the buffer.  Calls that share a workspace must
- *           be ordered on one stream.  When that size is 0 the workspace is not
- *           touched and may be NULL.
+ *           Its first 4096 bytes hold arrival counts; each count wraps back to
+ *           zero on the last arrival of every call, so one zero fill at
+ *           allocation serves every later call, for any descriptor, as long as
+ *           only sp_region_bwd writes the buffer.  The rest is scratch.  Calls
+ *           that share a workspace must be ordered on one stream: calls that
+ *           overlap in time race on it.  A call that never completes (its
+ *           kernel stopped part way) can leave counts that are not zero; the
+ *           next call on that workspace may then return dgamma / dbeta computed
+ *           from stale scratch, or NaN where a count is out of range.  Zero the
+ *           workspace again after such an event.  When the size is 0 the
+ *           workspace is not touched and may be NULL.
  *
  * dgamma / dbeta are fp32 sums in a fixed order, so repeated calls give the same
  * bits.  Two schedules exist, chosen from the shape (sp_region_bwd_schedule):
  * per-workgroup partial rows in the workspace summed by a second kernel, or
  * column workgroups inside the one launch, each summing a strip of columns over
  * a segment of rows; where a strip has several segments, the workgroup that
- * completes it adds them in segment order.
+ * completes it adds them in segment order.  That hand-over between workgroups
+ * uses device-scope atomic stores, a drain of the stores (s_waitcnt) and an
+ * integer atomic count, and relies on gfx950 performing device-scope accesses
+ * at the device's point of coherence; it uses no release/acquire fence.
  */
 int sp_region_bwd(const sp_desc_t* d, const void* dY, const void* h, const uint8_t* mask,
                   const float* mean, const float* rstd, const float* gamma,
@@ -165,7 +182,8 @@ int sp_region_bwd(const sp_desc_t* d, const void* dY, const void* h, const uint8
                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of workspace sp_region_bwd needs for this descriptor: 0 when it needs
- * none (then the workspace may be NULL) and on a bad descriptor. */
+ * none (then the workspace may be NULL) and on a bad descriptor.  Host only;
+ * the layout of the workspace is described at sp_region_bwd. */
 size_t sp_region_bwd_workspace_size(const sp_desc_t* d);
 
 /* The dgamma / dbeta schedule sp_region_bwd takes for this descriptor: 0 =
@@ -179,11 +197,21 @@ int sp_region_bwd_schedule(const sp_desc_t* d);
  * written once (fwd: T partial slabs, residual, h, y, mask, stats, gamma/beta;
  * bwd: dY, h, mask, stats, gamma, d_residual, dP, dgamma/dbeta; dR not counted;
  * no mask bytes with SP_FLAG_RECOMPUTE_MASK).
- * Returns SP_OK or the validation error of the descriptor.
+ *
+ *   "MiniMind-tron: SP optimisation", section 4.2.1: the pages count memory in
+ *   units of F = 2 bytes x S*B*H, one full-sequence bf16 [S,B,H] tensor (6 MiB
+ *   for B=2, S=2048, H=768).  One shard's tensor is F/T; a bf16 forward moves
+ *   (2T+7) bytes per shard element and the backward 9, so fwd = (T+3.5) F/T and
+ *   bwd = 4.5 F/T, plus the [R] statistics and [H] parameters.
+ *
+ * Returns SP_OK or the validation error of the descriptor; fwd_bytes and
+ * bwd_bytes must be non-NULL (SP_EINVAL).
  */
 int sp_region_traffic_bytes(const sp_desc_t* d, uint64_t* fwd_bytes, uint64_t* bwd_bytes);
 
-/* Static text for a status code (for SP_EHIP: the last HIP error seen by this thread). */
+/* Static text for a status code (for SP_EHIP: the text of the last launch error
+ * this thread saw from the library).  The library never calls hipGetLastError,
+ * so an error left pending by the caller's own work stays pending for it. */
 const char* sp_region_strerror(int status);
 
 /* Library version, major * 10000 + minor * 100 + patch. */

@@ -253,7 +253,7 @@ def test_workspace_size_scales_with_norm(lib):
     ((40, 5, 2000, 2, "f32", "ln"), 1),
     ((256, 1, 64, 2, "f32", "rms"), 1),
     ((8192, 2, 8192, 8, "bf16", "rms"), 0),    # 2048 rows of 8192
-    ((2048, 2, 768, 2, "bf16", "rms"), 0),     # 2048 rows of 768: small partial rows
+    ((2048, 2, 768, 2, "bf16", "rms"), 8),     # 2048 rows of 768: a 6 MiB second read, 8 segments
     ((32768, 1, 8192, 8, "bf16", "rms"), 0),
     ((4096, 4, 128, 4, "bf16", "ln"), 0),      # 4096 short rows
     ((16384, 1, 1024, 2, "bf16", "rms"), 0),   # 8192 rows of 1024
@@ -263,7 +263,9 @@ def test_workspace_size_scales_with_norm(lib):
     ((2056, 1, 2056, 2, "bf16", "ln"), 3),     # 1028 rows, a ragged last strip
     ((4100, 1, 1024, 2, "f32", "ln"), 9),      # 2050 fp32 rows: 9 segments of 228
     ((1040, 1, 20480, 2, "bf16", "rms"), 2),   # 520 long rows: 1024-lane rows always take columns
-    ((4096, 1, 16384, 2, "bf16", "ln"), 0),    # 2048 rows of 16384 (512 lanes x 4 chunks)
+    ((4096, 1, 16384, 2, "bf16", "ln"), 0),    # 2048 rows of 16384 (512 lanes x 4 chunks): 128 MiB second read
+    ((16384, 2, 512, 2, "bf16", "rms"), 0),    # 16384 rows of 512: too many segments
+    ((8192, 1, 4096, 2, "bf16", "rms"), 0),    # 4096 rows of 4096: a 64 MiB second read
     ((1040, 1, 65536, 2, "bf16", "ln"), 2),    # 520 of the longest rows: partial rows too large
 ])
 def test_backward_schedule_by_shape(lib, shape, schedule):

@@ -124,6 +124,13 @@ __device__ __forceinline__ u32x4 ld16(const void* base, int64_t byte_off) {
 #ifndef SP_COL_NT
 #define SP_COL_NT 0
 #endif
+#ifndef SP_ROWS_NT
+#define SP_ROWS_NT 1  // partial-row schedule: dY and h by streaming loads
+#endif
+#ifndef SP_COL_FIRST
+#define SP_COL_FIRST 1  // column workgroups take the first blockIdx values of the backward grid
+#endif
+constexpr bool kColFirst = SP_COL_FIRST != 0;
 template <bool NT>
 __device__ __forceinline__ u32x4 ld16_policy(const void* base, int64_t byte_off) {
     const u32x4* p = reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(base) + byte_off);
@@ -328,7 +335,8 @@ __device__ __forceinline__ void load_vec_f32(const float* p, int64_t idx, float 
 }
 
 // TT: number of partials fixed at compile time (0 = read a.T at run time).
-template <int DT, int TT, int TPR, int CPT, int BLOCK>
+// RPT: rows a row group takes at once (all their loads in flight together).
+template <int DT, int TT, int TPR, int CPT, int BLOCK, int RPT>
 __global__ __launch_bounds__(BLOCK) void sp_fwd_kernel(const FwdArgs a) {
     using A = Act<DT>;
     constexpr int E = A::E;
@@ -339,10 +347,7 @@ __global__ __launch_bounds__(BLOCK) void sp_fwd_kernel(const FwdArgs a) {
     const int tid = threadIdx.x;
     const int rg = tid / TPR;
     const int l = tid % TPR;
-    const int64_t row = (int64_t)blockIdx.x * RPW + rg;
-    const bool row_ok = row < a.R;
-    const int64_t rowc = row_ok ? row : a.R - 1;  // loads stay in bounds; stores are predicated
-    const int64_t row_elem = rowc * (int64_t)a.H;
+    const int64_t row0 = ((int64_t)blockIdx.x * RPW + rg) * RPT;
 
     int col[CPT];
     bool ok[CPT];
@@ -357,6 +362,11 @@ __global__ __launch_bounds__(BLOCK) void sp_fwd_kernel(const FwdArgs a) {
         // Rows too long for every partial chunk to sit in registers at once: the
         // chunks go through in batches of KB and h stays packed (16 bytes per
         // chunk) for the statistics and y.  Same arithmetic, same order.
+        static_assert(RPT == 1, "long rows are taken one at a time");
+        const int64_t row = row0;
+        const bool row_ok = row < a.R;
+        const int64_t rowc = row_ok ? row : a.R - 1;  // loads stay in bounds; stores are predicated
+        const int64_t row_elem = rowc * (int64_t)a.H;
         constexpr int KB = (TT > 0 && TT < 4) ? 2 : 1;
         u32x4 hp[CPT];
         float s1 = 0.0f;  // LayerNorm: sum of h; RMSNorm: sum of h^2
@@ -466,64 +476,84 @@ __global__ __launch_bounds__(BLOCK) void sp_fwd_kernel(const FwdArgs a) {
         return;
     }
 
-    // ---- loads: every partial chunk and the residual, issued together ----
-    float acc[CPT][E];
-    float res[CPT][E];
+    // ---- loads: every partial chunk and the residual of the RPT rows, issued together ----
+    bool rok[RPT];
+    int64_t relem[RPT];  // first element of each row (a valid row: loads stay in bounds)
+#pragma unroll
+    for (int p = 0; p < RPT; ++p) {
+        const int64_t r = row0 + p;
+        rok[p] = r < a.R;
+        relem[p] = (rok[p] ? r : a.R - 1) * (int64_t)a.H;
+    }
+    float acc[RPT][CPT][E];
+    float res[RPT][CPT][E];
     // With few partials the generator is a visible share of the work: its flags
     // (one bit per element) are then made while the loads are in flight.
     constexpr bool kEarlyFlags = SP_EARLY_FLAGS && TT > 0 && TT <= 2;
-    uint32_t kbits[CPT];
+    uint32_t kbits[RPT][CPT];
     if constexpr (TT > 0) {
-        u32x4 pv[CPT][TT];
-        u32x4 rv[CPT];
+        u32x4 pv[RPT][CPT][TT];
+        u32x4 rv[RPT][CPT];
 #pragma unroll
-        for (int k = 0; k < CPT; ++k) {
-            const int64_t off = (row_elem + col[k]) * EB;
+        for (int p = 0; p < RPT; ++p)
 #pragma unroll
-            for (int t = 0; t < TT; ++t) pv[k][t] = ld16(a.P[t], off);
-            rv[k] = ld16(a.residual, off);
-        }
+            for (int k = 0; k < CPT; ++k) {
+                const int64_t off = (relem[p] + col[k]) * EB;
+#pragma unroll
+                for (int t = 0; t < TT; ++t) pv[p][k][t] = ld16(a.P[t], off);
+                rv[p][k] = ld16(a.residual, off);
+            }
         if constexpr (kEarlyFlags) {
 #pragma unroll
+            for (int p = 0; p < RPT; ++p)
+#pragma unroll
+                for (int k = 0; k < CPT; ++k) {
+                    bool kf[E];
+                    keep_flags<E>(a.base + (uint64_t)(relem[p] + col[k]), a.thr, a.key0, a.key1, kf);
+                    kbits[p][k] = 0;
+#pragma unroll
+                    for (int e = 0; e < E; ++e) kbits[p][k] |= (uint32_t)kf[e] << e;
+                }
+        }
+#pragma unroll
+        for (int p = 0; p < RPT; ++p)
+#pragma unroll
             for (int k = 0; k < CPT; ++k) {
-                bool kf[E];
-                keep_flags<E>(a.base + (uint64_t)(row_elem + col[k]), a.thr, a.key0, a.key1, kf);
-                kbits[k] = 0;
+                A::unpack(pv[p][k][0], acc[p][k]);
 #pragma unroll
-                for (int e = 0; e < E; ++e) kbits[k] |= (uint32_t)kf[e] << e;
+                for (int t = 1; t < TT; ++t) {
+                    float f[E];
+                    A::unpack(pv[p][k][t], f);
+#pragma unroll
+                    for (int e = 0; e < E; ++e) acc[p][k][e] = acc[p][k][e] + f[e];
+                }
+                A::unpack(rv[p][k], res[p][k]);
             }
-        }
-#pragma unroll
-        for (int k = 0; k < CPT; ++k) {
-            A::unpack(pv[k][0], acc[k]);
-#pragma unroll
-            for (int t = 1; t < TT; ++t) {
-                float f[E];
-                A::unpack(pv[k][t], f);
-#pragma unroll
-                for (int e = 0; e < E; ++e) acc[k][e] = acc[k][e] + f[e];
-            }
-            A::unpack(rv[k], res[k]);
-        }
     } else {
-        u32x4 rv[CPT];
+        u32x4 rv[RPT][CPT];
 #pragma unroll
-        for (int k = 0; k < CPT; ++k) {
-            const int64_t off = (row_elem + col[k]) * EB;
-            rv[k] = ld16(a.residual, off);
-            A::unpack(ld16(a.P[0], off), acc[k]);
-        }
+        for (int p = 0; p < RPT; ++p)
+#pragma unroll
+            for (int k = 0; k < CPT; ++k) {
+                const int64_t off = (relem[p] + col[k]) * EB;
+                rv[p][k] = ld16(a.residual, off);
+                A::unpack(ld16(a.P[0], off), acc[p][k]);
+            }
         for (int t = 1; t < a.T; ++t) {
 #pragma unroll
-            for (int k = 0; k < CPT; ++k) {
-                float f[E];
-                A::unpack(ld16(a.P[t], (row_elem + col[k]) * EB), f);
+            for (int p = 0; p < RPT; ++p)
 #pragma unroll
-                for (int e = 0; e < E; ++e) acc[k][e] = acc[k][e] + f[e];
-            }
+                for (int k = 0; k < CPT; ++k) {
+                    float f[E];
+                    A::unpack(ld16(a.P[t], (relem[p] + col[k]) * EB), f);
+#pragma unroll
+                    for (int e = 0; e < E; ++e) acc[p][k][e] = acc[p][k][e] + f[e];
+                }
         }
 #pragma unroll
-        for (int k = 0; k < CPT; ++k) A::unpack(rv[k], res[k]);
+        for (int p = 0; p < RPT; ++p)
+#pragma unroll
+            for (int k = 0; k < CPT; ++k) A::unpack(rv[p][k], res[p][k]);
     }
 
     // gamma / beta for the normalisation, loaded early
@@ -535,76 +565,96 @@ __global__ __launch_bounds__(BLOCK) void sp_fwd_kernel(const FwdArgs a) {
     }
 
     // ---- dropout + residual add, one rounding of h ----
-    float hv[CPT][E];
+    float hv[RPT][CPT][E];
 #pragma unroll
-    for (int k = 0; k < CPT; ++k) {
-        const int64_t idx = row_elem + col[k];
-        bool keep[E];
-        if constexpr (kEarlyFlags) {
+    for (int p = 0; p < RPT; ++p)
 #pragma unroll
-            for (int e = 0; e < E; ++e) keep[e] = (kbits[k] >> e) & 1u;
-        } else {
-            keep_flags<E>(a.base + (uint64_t)idx, a.thr, a.key0, a.key1, keep);
+        for (int k = 0; k < CPT; ++k) {
+            const int64_t idx = relem[p] + col[k];
+            bool keep[E];
+            if constexpr (kEarlyFlags) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) keep[e] = (kbits[p][k] >> e) & 1u;
+            } else {
+                keep_flags<E>(a.base + (uint64_t)idx, a.thr, a.key0, a.key1, keep);
+            }
+            float hf[E];
+            residual_add<E>(acc[p][k], res[p][k], keep, a.scale, hf);
+            const u32x4 hp = A::pack(hf);
+            A::unpack(hp, hv[p][k]);  // the rounded h the norm sees
+            if (rok[p] && ok[k]) {
+                st16(a.h, idx * EB, hp);
+                if (a.mask) *reinterpret_cast<typename MW::type*>(a.mask + idx) = MW::make(keep);
+            }
         }
-        float hf[E];
-        residual_add<E>(acc[k], res[k], keep, a.scale, hf);
-        const u32x4 hp = A::pack(hf);
-        A::unpack(hp, hv[k]);  // the rounded h the norm sees
-        if (row_ok && ok[k]) {
-            st16(a.h, idx * EB, hp);
-            if (a.mask) *reinterpret_cast<typename MW::type*>(a.mask + idx) = MW::make(keep);
-        }
-    }
 
-    // ---- per-token statistics ----
-    float mu = 0.0f, rs;
+    // ---- per-token statistics (the RPT rows' sums reduced together) ----
+    float mu[RPT], rs[RPT];
     if (a.norm == SP_LAYERNORM) {
-        float s[1] = {0.0f};
+        float s[RPT];
 #pragma unroll
-        for (int k = 0; k < CPT; ++k)
-            if (ok[k])
+        for (int p = 0; p < RPT; ++p) {
+            s[p] = 0.0f;
 #pragma unroll
-                for (int e = 0; e < E; ++e) s[0] += hv[k][e];
-        group_sum<TPR, BLOCK, 1>(s);
-        mu = s[0] * a.inv_h;
-        float q[1] = {0.0f};
+            for (int k = 0; k < CPT; ++k)
+                if (ok[k])
 #pragma unroll
-        for (int k = 0; k < CPT; ++k)
-            if (ok[k])
+                    for (int e = 0; e < E; ++e) s[p] += hv[p][k][e];
+        }
+        group_sum<TPR, BLOCK, RPT>(s);
+        float q[RPT];
 #pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const float dlt = hv[k][e] - mu;
-                    q[0] += dlt * dlt;
-                }
-        group_sum<TPR, BLOCK, 1, false>(q);
-        rs = rsqrtf(q[0] * a.inv_h + a.eps);
+        for (int p = 0; p < RPT; ++p) {
+            mu[p] = s[p] * a.inv_h;
+            q[p] = 0.0f;
+#pragma unroll
+            for (int k = 0; k < CPT; ++k)
+                if (ok[k])
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        const float dlt = hv[p][k][e] - mu[p];
+                        q[p] += dlt * dlt;
+                    }
+        }
+        group_sum<TPR, BLOCK, RPT, false>(q);
+#pragma unroll
+        for (int p = 0; p < RPT; ++p) rs[p] = rsqrtf(q[p] * a.inv_h + a.eps);
     } else {
-        float q[1] = {0.0f};
+        float q[RPT];
 #pragma unroll
-        for (int k = 0; k < CPT; ++k)
-            if (ok[k])
+        for (int p = 0; p < RPT; ++p) {
+            mu[p] = 0.0f;
+            q[p] = 0.0f;
 #pragma unroll
-                for (int e = 0; e < E; ++e) q[0] += hv[k][e] * hv[k][e];
-        group_sum<TPR, BLOCK, 1, false>(q);
-        rs = rsqrtf(q[0] * a.inv_h + a.eps);
+            for (int k = 0; k < CPT; ++k)
+                if (ok[k])
+#pragma unroll
+                    for (int e = 0; e < E; ++e) q[p] += hv[p][k][e] * hv[p][k][e];
+        }
+        group_sum<TPR, BLOCK, RPT, false>(q);
+#pragma unroll
+        for (int p = 0; p < RPT; ++p) rs[p] = rsqrtf(q[p] * a.inv_h + a.eps);
     }
 
     // ---- y = gamma * xhat (+ beta), one rounding ----
 #pragma unroll
-    for (int k = 0; k < CPT; ++k) {
-        float yv[E];
-        if (a.norm == SP_LAYERNORM) {
+    for (int p = 0; p < RPT; ++p) {
 #pragma unroll
-            for (int e = 0; e < E; ++e) yv[e] = gam[k][e] * ((hv[k][e] - mu) * rs) + bet[k][e];
-        } else {
+        for (int k = 0; k < CPT; ++k) {
+            float yv[E];
+            if (a.norm == SP_LAYERNORM) {
 #pragma unroll
-            for (int e = 0; e < E; ++e) yv[e] = gam[k][e] * (hv[k][e] * rs);
+                for (int e = 0; e < E; ++e) yv[e] = gam[k][e] * ((hv[p][k][e] - mu[p]) * rs[p]) + bet[k][e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e) yv[e] = gam[k][e] * (hv[p][k][e] * rs[p]);
+            }
+            if (rok[p] && ok[k]) st16(a.y, (relem[p] + col[k]) * EB, A::pack(yv));
         }
-        if (row_ok && ok[k]) st16(a.y, (row_elem + col[k]) * EB, A::pack(yv));
-    }
-    if (row_ok && l == 0) {
-        a.rstd[row] = rs;
-        if (a.norm == SP_LAYERNORM) a.mean[row] = mu;
+        if (rok[p] && l == 0) {
+            a.rstd[row0 + p] = rs[p];
+            if (a.norm == SP_LAYERNORM) a.mean[row0 + p] = mu[p];
+        }
     }
 }
 
@@ -690,8 +740,8 @@ __device__ __forceinline__ void bwd_load_step(const BwdArgs& a, int64_t row0, in
 // order, then the offsets are added in a fixed tree (lane butterfly inside a
 // wavefront, wavefronts in order through LDS).  With one segment per strip
 // that sum is dgamma.  With several, each segment publishes its sums and counts
-// itself in; the workgroup that completes the strip adds the segments in
-// segment order and sets the count back to zero.  The order of every addition
+// itself in (the count wraps back to zero on the last arrival); the workgroup
+// that completes the strip adds the segments in segment order.  The order of every addition
 // is fixed, whichever workgroup finishes last.  Needs no second launch, at the
 // cost of reading dY and h a second time.
 #ifndef SP_COL_BATCH
@@ -716,7 +766,7 @@ __device__ __forceinline__ void bwd_columns(const BwdArgs& a, int wg) {
     constexpr int kB = col_batch(BLOCK);  // steps whose loads are in flight together
     constexpr int NW = BLOCK / kWave;
     __shared__ float cred[NW][NACC][kSeg * E];
-    __shared__ uint32_t completes;
+    __shared__ uint32_t arrived;
 
     const int strip = wg % a.col_strips;
     const int seg = wg / a.col_strips;
@@ -800,33 +850,54 @@ __device__ __forceinline__ void bwd_columns(const BwdArgs& a, int wg) {
         return;
     }
     // Several segments: publish this one's sums, then count in.  The sums go
-    // out as device-scope stores, which are coherent across the XCDs' L2
-    // caches once complete; every wave drains its stores before the barrier,
-    // so they are complete before the count is taken, and the workgroup that
-    // completes the strip reads them back with device-scope loads.  (A device
-    // fence would instead write back every dirty line of the L2, the
-    // d_residual and dP tiles of the whole XCD included: on 2048 rows of 768
-    // the backward took 20.5 us with fences, 8.7 us without.)
+    // out as device-scope (agent) atomic stores and every wave drains them
+    // (s_waitcnt) before the barrier, so they have reached the device's point of
+    // coherence before the count is taken; the workgroup that completes the
+    // strip reads them back with device-scope atomic loads, issued after its
+    // count returned.  This relies on gfx950 performing device-scope stores and
+    // loads at that point (they bypass the XCD-private caches), not on a
+    // release/acquire pair: a device fence would write back every dirty line of
+    // the XCD's L2, the d_residual and dP tiles included (on 2048 rows of 768
+    // the backward took 20.5 us with fences, 8.7 us without).
     float* const part = a.ws + ((int64_t)seg * NACC + acc) * a.H + gcol;
     if (live) __hip_atomic_store(part, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (tid == 0) {
-        const uint32_t before = atomicAdd(a.col_count + strip, 1u);
-        completes = before == (uint32_t)(nseg - 1);
-    }
+    // The count wraps to zero on the strip's last arrival (atomicInc with bound
+    // nseg - 1), so every completed call leaves it at zero.  A count above
+    // nseg - 1 can only be left by a call that never completed, or by calls of
+    // different shapes racing on one workspace: the strip's outputs are then
+    // NaN instead of sums read from segments that may be stale.
+    if (tid == 0) arrived = atomicInc(a.col_count + strip, (uint32_t)(nseg - 1));
     __syncthreads();
-    if (!completes) return;  // uniform over the workgroup
+    const uint32_t before = arrived;  // uniform over the workgroup
+    if (before < (uint32_t)(nseg - 1)) return;
+    if (before > (uint32_t)(nseg - 1)) {
+        if (live) out[gcol] = __builtin_nanf("");
+        return;
+    }
     if (live) {
+        // every segment's sum, in segment order; the loads of a batch are in
+        // flight together
         const float* src = a.ws + (int64_t)acc * a.H + gcol;
-        float t = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        for (int q = 1; q < nseg; ++q)
-            t += __hip_atomic_load(src + (int64_t)q * NACC * a.H, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int64_t stride = (int64_t)NACC * a.H;
+        constexpr int kRead = 8;
+        float t = 0.0f;
+        for (int q0 = 0; q0 < nseg; q0 += kRead) {
+            float sv[kRead];
+#pragma unroll
+            for (int b = 0; b < kRead; ++b)
+                sv[b] = q0 + b < nseg
+                            ? __hip_atomic_load(src + (q0 + b) * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                            : 0.0f;
+#pragma unroll
+            for (int b = 0; b < kRead; ++b) {
+                if (q0 + b == 0) t = sv[b];
+                else if (q0 + b < nseg) t += sv[b];
+            }
+        }
         out[gcol] = t;
     }
-    // every segment of this strip has counted in: no other workgroup of the
-    // launch touches the count again
-    if (tid == 0) __hip_atomic_store(a.col_count + strip, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // A workgroup holds RG row groups of TPR lanes and walks a tile of
@@ -852,14 +923,18 @@ __global__ __launch_bounds__(RG* TPR) void sp_bwd_kernel(const BwdArgs a) {
     const int tid = threadIdx.x;
     const int rg = tid / TPR;
     const int l = tid % TPR;
+    // the column workgroups come first in the grid, or after the row workgroups
+    const int nrow_wg = (int)gridDim.x - a.col_blocks;
+    const int col_wg = kColFirst ? (int)blockIdx.x : (int)blockIdx.x - nrow_wg;
+    const int row_wg = kColFirst ? (int)blockIdx.x - a.col_blocks : (int)blockIdx.x;
     if constexpr (COLS) {
-        if ((int)blockIdx.x < a.col_blocks) {  // grid-uniform choice per workgroup
-            bwd_columns<DT, LN, BLOCK>(a, (int)blockIdx.x);
+        if (col_wg >= 0 && col_wg < a.col_blocks) {  // uniform over the workgroup
+            bwd_columns<DT, LN, BLOCK>(a, col_wg);
             return;
         }
     }
     constexpr bool partial_rows = !COLS;
-    const int64_t row_begin = (int64_t)(blockIdx.x - a.col_blocks) * a.rows_per_block;
+    const int64_t row_begin = (int64_t)row_wg * a.rows_per_block;
     const int64_t row_end = min(row_begin + a.rows_per_block, a.R);
     const int iters = (int)((a.rows_per_block + STEP - 1) / STEP);  // uniform over the grid
 
@@ -890,9 +965,9 @@ __global__ __launch_bounds__(RG* TPR) void sp_bwd_kernel(const BwdArgs a) {
     }
 
     BwdRow<CPT, E> rows[PF];
-    // streaming loads unless the column workgroups read dY and h again
+    // streaming loads of dY and h unless the column workgroups read them again
     auto load_step = [&](int64_t r0, BwdRow<CPT, E>(&dst)[PF]) {
-        bwd_load_step<DT, LN, CPT, PF, HAS_DR, REGEN, !COLS>(a, r0, row_end, col, dst);
+        bwd_load_step<DT, LN, CPT, PF, HAS_DR, REGEN, !COLS && SP_ROWS_NT>(a, r0, row_end, col, dst);
     };
     // regenerated keep flags (one bit per element), made right after a step's
     // loads are issued so that the generator runs while they are in flight;
@@ -997,7 +1072,7 @@ __global__ __launch_bounds__(RG* TPR) void sp_bwd_kernel(const BwdArgs a) {
 
     // ---- this workgroup's partial dgamma / dbeta row ----
     if constexpr (COLS) return;
-    float* out = a.ws + (int64_t)(blockIdx.x - a.col_blocks) * NACC * a.H;
+    float* out = a.ws + (int64_t)row_wg * NACC * a.H;
     if constexpr (RG == 1) {
 #pragma unroll
         for (int k = 0; k < CPT; ++k) {
@@ -1135,6 +1210,9 @@ constexpr int block_of(int tpr) { return tpr <= kWave ? kSubWaveBlock : tpr; }
 #ifndef SP_FWD_LAYOUT
 #define SP_FWD_LAYOUT -1
 #endif
+#ifndef SP_FWD_RPT
+#define SP_FWD_RPT 1  // rows per forward row group (tuning builds: 2)
+#endif
 #ifndef SP_BWD_VARIANT
 #define SP_BWD_VARIANT -1
 #endif
@@ -1178,16 +1256,22 @@ constexpr int64_t col_row_blocks(int block) { return block <= 256 ? SP_COL_ROW_B
 typedef void (*FwdKernel)(FwdArgs);
 typedef void (*BwdKernel)(BwdArgs);
 
-#define SP_FWD_ENTRY(TPR, CPT, LIMIT, DT, TT) &sp_fwd_kernel<DT, TT, TPR, CPT, block_of(TPR)>
+// Rows too long to keep every partial chunk in registers are taken one at a time,
+// in batches of chunks; every other layout may take several rows per row group.
+constexpr bool fwd_batched(int tpr, int cpt) { return block_of(tpr) > 512 && cpt > 2; }
+constexpr int fwd_rpt(int tpr, int cpt, int rpt) { return fwd_batched(tpr, cpt) ? 1 : rpt; }
+#define SP_FWD_ENTRY(TPR, CPT, LIMIT, DT, TT, RPT) \
+    &sp_fwd_kernel<DT, TT, TPR, CPT, block_of(TPR), fwd_rpt(TPR, CPT, RPT)>
 #define SP_BWD_ENTRY(TPR, CPT, RG, PF, BLOCKS, DT, NORM, HDR, REGEN, COLS) \
     &sp_bwd_kernel<DT, NORM, TPR, CPT, RG, PF, HDR, REGEN, COLS>
 
+// [fixed T: run time, 1, 2, 4, 8][layout]
 const FwdKernel kFwdBf16[5][kNumLayouts] = {
-    {SP_LAYOUT_LIST(SP_FWD_ENTRY, SP_BF16, 0)}, {SP_LAYOUT_LIST(SP_FWD_ENTRY, SP_BF16, 1)},
-    {SP_LAYOUT_LIST(SP_FWD_ENTRY, SP_BF16, 2)}, {SP_LAYOUT_LIST(SP_FWD_ENTRY, SP_BF16, 4)},
-    {SP_LAYOUT_LIST(SP_FWD_ENTRY, SP_BF16, 8)},
+    {SP_LAYOUT_LIST(SP_FWD_ENTRY, SP_BF16, 0, SP_FWD_RPT)}, {SP_LAYOUT_LIST(SP_FWD_ENTRY, SP_BF16, 1, SP_FWD_RPT)},
+    {SP_LAYOUT_LIST(SP_FWD_ENTRY, SP_BF16, 2, SP_FWD_RPT)}, {SP_LAYOUT_LIST(SP_FWD_ENTRY, SP_BF16, 4, SP_FWD_RPT)},
+    {SP_LAYOUT_LIST(SP_FWD_ENTRY, SP_BF16, 8, SP_FWD_RPT)},
 };
-const FwdKernel kFwdF32[kNumLayouts] = {SP_LAYOUT_LIST(SP_FWD_ENTRY, SP_F32, 0)};
+const FwdKernel kFwdF32[kNumLayouts] = {SP_LAYOUT_LIST(SP_FWD_ENTRY, SP_F32, 0, SP_FWD_RPT)};
 // [dtype][norm][has dR][mask regenerated][column schedule][variant]
 #define SP_BWD_BY_REGEN(DT, NORM, HDR, REGEN)                      \
     {{SP_BWD_LIST(SP_BWD_ENTRY, DT, NORM, HDR, REGEN, false)},     \
@@ -1303,30 +1387,36 @@ static_assert((size_t)SP_MAX_H_BYTES / 16 / kSeg * sizeof(uint32_t) <= kWsCountB
 #ifndef SP_BWD_DG
 #define SP_BWD_DG 0
 #endif
-// The finish launch costs about as much time as moving this many bytes.
-constexpr int64_t kFinishLaunchBytes = (int64_t)16 << 20;
-
 // Rows a column workgroup takes in one batch of loads: one segment at most, so
 // that no column walk becomes the critical path of the launch.
 constexpr int64_t col_segment_rows(int block) { return (int64_t)(block / kSeg) * col_batch(block); }
 
-// Partial rows smaller than this are cheaper than the arrival chain of
-// several column segments (store, count, read back).
-constexpr int64_t kSegMinPartialBytes = (int64_t)2 << 20;
-
-// Column workgroups read dY and h a second time (2 R H e bytes) but need no
-// partial rows (2 G nacc H 4 bytes written and read back) and no second launch.
-// Rows past one segment add the segments' arrival chain, which costs about as
-// much as the finish launch: several segments pay only where the partial rows
-// are large.  Rows of 1024-lane workgroups always take columns: there the
-// per-lane dgamma / dbeta accumulators of the partial-row schedule spill.
-bool use_columns(int64_t R, int64_t H, int eb, int64_t G, int nacc, int block) {
+// Column workgroups read dY and h a second time (2 R H e bytes), but need no
+// partial rows and no second launch; a strip's segments are joined inside the
+// launch by the workgroup that completes it.  That pays where the second read
+// is small enough to be served largely from the caches, a row holds a few
+// strips and the rows fit in a few segments.  Measured on bf16 shards, over
+// buffer sets larger than the Infinity Cache (backward us, partial rows ->
+// columns): 2048 x 768 RMS 7.8 -> 7.3; a second read of 67 MB (2048 x 8192
+// RMS) 36.8 -> 38.3 and of 134 MB (4096 x 8192 RMS) 65.3 -> 77.2 keep the
+// partial rows; so do rows of two strips (4096 x 128 LN 6.3 / 6.5) and many
+// segments (8192 x 1024 RMS, 32 segments: 19.3 / 19.4), unless all rows fit
+// in one segment.  Rows of 1024-lane workgroups always take columns: there the
+// partial-row schedule's per-lane dgamma / dbeta accumulators spill.
+#ifndef SP_COL_MIN_STRIPS
+#define SP_COL_MIN_STRIPS 4
+#endif
+#ifndef SP_COL_MAX_SEGS
+#define SP_COL_MAX_SEGS 16
+#endif
+constexpr int64_t kColMaxReread = (int64_t)32 << 20;
+bool use_columns(int64_t R, int64_t H, int eb, int block) {
     if (SP_BWD_DG == 1 || R == 0) return false;
     if (SP_BWD_DG == 2 || block > 512) return true;
-    const int64_t reread = 2 * R * H * eb, partial = 2 * G * nacc * H * 4;
-    if (R <= col_segment_rows(block)) return reread <= partial + kFinishLaunchBytes;
-    if (partial < kSegMinPartialBytes) return false;
-    return reread <= partial + kFinishLaunchBytes;
+    const int64_t strips = (H * eb / 16 + kSeg - 1) / kSeg;
+    const int64_t segs = (R + col_segment_rows(block) - 1) / col_segment_rows(block);
+    if (segs == 1) return true;  // no workspace, no second launch, a small re-read
+    return strips >= SP_COL_MIN_STRIPS && segs <= SP_COL_MAX_SEGS && 2 * R * H * eb <= kColMaxReread;
 }
 
 BwdPlan plan_bwd(const sp_desc_t* d) {
@@ -1347,7 +1437,7 @@ BwdPlan plan_bwd(const sp_desc_t* d) {
         p.blocks = R > 0 ? (R + rpb - 1) / rpb : 0;
     };
     tile_rows(SP_BWD_TARGET_BLOCKS > 0 ? SP_BWD_TARGET_BLOCKS : kBwdVariants[p.variant].blocks);
-    if (use_columns(R, H, elem_bytes(d->dtype), p.blocks, p.nacc, p.block)) {
+    if (use_columns(R, H, elem_bytes(d->dtype), p.block)) {
         // Rows split into equal segments of at most one batch each.
         const int64_t most = col_segment_rows(p.block);
         int64_t segs = (R + most - 1) / most;
@@ -1377,6 +1467,14 @@ BwdPlan plan_bwd(const sp_desc_t* d) {
 int record_hip(hipError_t e) {
     snprintf(g_hip_error, sizeof(g_hip_error), "HIP error %d: %s", (int)e, hipGetErrorString(e));
     return SP_EHIP;
+}
+
+// Enqueue a kernel; its status comes from the launch call itself, so an error
+// that earlier work left pending for the caller is neither cleared nor taken
+// for this launch's.
+int launch(const void* kernel, unsigned grid, unsigned block, size_t lds, void* stream, void** args) {
+    const hipError_t e = hipLaunchKernel(kernel, dim3(grid), dim3(block), args, lds, (hipStream_t)stream);
+    return e == hipSuccess ? SP_OK : record_hip(e);
 }
 
 }  // namespace
@@ -1502,14 +1600,12 @@ extern "C" int sp_region_fwd(const sp_desc_t* d, const void* const* P, const voi
     if (li < 0) return SP_ESHAPE;
     const Layout L = kLayouts[li];
     const int block = block_of(L.tpr);
-    const int rpw = block / L.tpr;
-    const int64_t grid = (R + rpw - 1) / rpw;
+    const int64_t rows_per_wg = (int64_t)(block / L.tpr) * fwd_rpt(L.tpr, L.cpt, SP_FWD_RPT);
+    const int64_t grid = (R + rows_per_wg - 1) / rows_per_wg;
     if (grid > INT32_MAX) return SP_ESHAPE;
     const FwdKernel k = d->dtype == SP_BF16 ? kFwdBf16[fwd_tt_index(d->T)][li] : kFwdF32[li];
-    (void)hipGetLastError();
-    hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(block), 0, (hipStream_t)stream, a);
-    const hipError_t e = hipGetLastError();
-    return e == hipSuccess ? SP_OK : record_hip(e);
+    void* args[] = {&a};
+    return launch((const void*)k, (unsigned)grid, (unsigned)block, 0, stream, args);
 }
 
 extern "C" int sp_region_bwd(const sp_desc_t* d, const void* dY, const void* h, const uint8_t* mask,
@@ -1589,21 +1685,21 @@ extern "C" int sp_region_bwd(const sp_desc_t* d, const void* dY, const void* h, 
 
     if (plan.variant < 0) return SP_ESHAPE;
     if (plan.blocks + plan.col_blocks > INT32_MAX) return SP_ESHAPE;
-    (void)hipGetLastError();
     if (plan.blocks > 0) {
         const BwdKernel k = kBwd[d->dtype == SP_BF16 ? 1 : 0][d->norm == SP_LAYERNORM ? 1 : 0][dR ? 1 : 0]
                                 [regen ? 1 : 0][plan.col_blocks > 0 ? 1 : 0][plan.variant];
-        hipLaunchKernelGGL(k, dim3((unsigned)(plan.col_blocks + plan.blocks)), dim3(plan.block),
-                           (unsigned)plan.lds_bytes, (hipStream_t)stream, a);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return record_hip(e);
+        void* args[] = {&a};
+        rc = launch((const void*)k, (unsigned)(plan.col_blocks + plan.blocks), (unsigned)plan.block,
+                    plan.lds_bytes, stream, args);
+        if (rc != SP_OK) return rc;
     }
     if (plan.col_blocks > 0) return SP_OK;  // the column workgroups wrote dgamma / dbeta
     const int ncols = plan.nacc * (int)H;
     const unsigned fin_grid = (unsigned)((ncols / 4 + kFinGroups - 1) / kFinGroups);
-    hipLaunchKernelGGL(sp_dgamma_finish_kernel, dim3(fin_grid), dim3(kFinGroups * kFinSlices), 0,
-                       (hipStream_t)stream, (const float*)a.ws, plan.blocks, (int32_t)H,
-                       (int32_t)plan.nacc, dgamma, dbeta);
-    const hipError_t e = hipGetLastError();
-    return e == hipSuccess ? SP_OK : record_hip(e);
+    const float* fin_ws = a.ws;
+    int64_t fin_g = plan.blocks;
+    int32_t fin_h = (int32_t)H, fin_nacc = (int32_t)plan.nacc;
+    void* args[] = {&fin_ws, &fin_g, &fin_h, &fin_nacc, &dgamma, &dbeta};
+    return launch((const void*)sp_dgamma_finish_kernel, fin_grid, (unsigned)(kFinGroups * kFinSlices), 0, stream,
+                  args);
 }
