@@ -89,11 +89,14 @@ def make_desc(S, B, H, T, j, dtype="bf16", norm="rms", eps=1e-6, p=0.1, seed=123
 
 
 def _ptr(x):
-    """Device address of a tensor (or an int address / None)."""
+    """Device address of a tensor (or an int address / None).  A tensor must be
+    in GPU memory: the library would otherwise read a host address."""
     if x is None:
         return None
     if isinstance(x, int):
         return x
+    if not x.is_cuda:
+        raise ValueError("tensor arguments must be in GPU memory")
     return x.data_ptr()
 
 
@@ -162,45 +165,112 @@ def _act_dtype(desc):
     return torch.bfloat16 if desc.dtype == SP_BF16 else torch.float32
 
 
+def _need(name, t, dtype, numel, device):
+    """Reject what the library cannot check itself: a missing tensor, the wrong
+    dtype, device or size, or a non-contiguous layout."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() != numel:
+        raise ValueError(f"{name} must have {numel} elements, got {t.numel()}")
+
+
+def _on_stream(stream):
+    """The torch stream to allocate and launch on (torch's current one by default)."""
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return torch.cuda.ExternalStream(stream)
+    return stream
+
+
 def forward(desc, P, residual, gamma, beta=None, stream=None):
     """P: T full [S,B,H] device tensors; residual: the shard (R*H elements).
     Returns dict h, y, mask (None with SP_FLAG_RECOMPUTE_MASK), mean (None for
-    RMSNorm), rstd."""
+    RMSNorm), rstd.  Outputs are allocated, and the kernel enqueued, on `stream`
+    (torch's current stream by default)."""
     import torch
-    dev = residual.device
     R, H = desc.R, desc.H
     act = _act_dtype(desc)
+    if len(P) != desc.T:
+        raise ValueError(f"P holds {len(P)} partials, the descriptor says T = {desc.T}")
+    dev = residual.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be in GPU memory")
+    for t, x in enumerate(P):
+        _need(f"P[{t}]", x, act, desc.S * desc.B * H, dev)
+    _need("residual", residual, act, R * H, dev)
+    _need("gamma", gamma, torch.float32, H, dev)
+    if desc.norm == SP_LAYERNORM:
+        _need("beta", beta, torch.float32, H, dev)
+    elif beta is not None:
+        raise ValueError("beta must be None for RMSNorm")
     keep_mask = not (desc.flags & SP_FLAG_RECOMPUTE_MASK)
-    out = {
-        "h": torch.empty((R, H), dtype=act, device=dev),
-        "y": torch.empty((R, H), dtype=act, device=dev),
-        "mask": torch.empty((R, H), dtype=torch.uint8, device=dev) if keep_mask else None,
-        "mean": torch.empty(R, dtype=torch.float32, device=dev) if desc.norm == SP_LAYERNORM else None,
-        "rstd": torch.empty(R, dtype=torch.float32, device=dev),
-    }
-    _check(sp_region_fwd(desc, P, residual, gamma, beta, out["h"], out["y"], out["mask"],
-                         out["mean"], out["rstd"], stream))
+    s = _on_stream(stream)
+    with torch.cuda.stream(s):
+        out = {
+            "h": torch.empty((R, H), dtype=act, device=dev),
+            "y": torch.empty((R, H), dtype=act, device=dev),
+            "mask": torch.empty((R, H), dtype=torch.uint8, device=dev) if keep_mask else None,
+            "mean": torch.empty(R, dtype=torch.float32, device=dev) if desc.norm == SP_LAYERNORM else None,
+            "rstd": torch.empty(R, dtype=torch.float32, device=dev),
+        }
+        _check(sp_region_fwd(desc, P, residual, gamma, beta, out["h"], out["y"], out["mask"],
+                             out["mean"], out["rstd"], s))
     return out
 
 
 def backward(desc, dY, h, mask, mean, rstd, gamma, dR=None, workspace=None, stream=None):
     """Returns dict d_res, dP, dgamma, dbeta (None for RMSNorm).  A workspace
-    passed in must have been zero-filled before its first use."""
+    passed in must have been zero-filled before its first use; without one, a
+    zero-filled workspace is allocated on `stream`, where the outputs are
+    allocated and the kernels enqueued (torch's current stream by default)."""
     import torch
-    dev = dY.device
     R, H = desc.R, desc.H
     act = _act_dtype(desc)
+    dev = dY.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be in GPU memory")
+    _need("dY", dY, act, R * H, dev)
+    _need("h", h, act, R * H, dev)
+    if desc.flags & SP_FLAG_RECOMPUTE_MASK:
+        if mask is not None:
+            raise ValueError("mask must be None with SP_FLAG_RECOMPUTE_MASK")
+    else:
+        _need("mask", mask, torch.uint8, R * H, dev)
+    if desc.norm == SP_LAYERNORM:
+        _need("mean", mean, torch.float32, R, dev)
+    elif mean is not None:
+        raise ValueError("mean must be None for RMSNorm")
+    _need("rstd", rstd, torch.float32, R, dev)
+    _need("gamma", gamma, torch.float32, H, dev)
+    if dR is not None:
+        _need("dR", dR, act, R * H, dev)
     ws_bytes = sp_region_bwd_workspace_size(desc)
-    if workspace is None:
-        workspace = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-    out = {
-        "d_res": torch.empty((R, H), dtype=act, device=dev),
-        "dP": torch.empty((R, H), dtype=act, device=dev),
-        "dgamma": torch.empty(H, dtype=torch.float32, device=dev),
-        "dbeta": torch.empty(H, dtype=torch.float32, device=dev) if desc.norm == SP_LAYERNORM else None,
-    }
-    _check(sp_region_bwd(desc, dY, h, mask, mean, rstd, gamma, dR, out["d_res"], out["dP"],
-                         out["dgamma"], out["dbeta"], workspace, workspace.numel(), stream))
+    if workspace is not None:
+        if workspace.device != dev or not workspace.is_contiguous():
+            raise ValueError(f"workspace must be a contiguous tensor on {dev}")
+        if workspace.numel() * workspace.element_size() < ws_bytes:
+            raise ValueError(f"workspace must hold at least {ws_bytes} bytes")
+    s = _on_stream(stream)
+    with torch.cuda.stream(s):
+        if workspace is None:
+            workspace = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+        out = {
+            "d_res": torch.empty((R, H), dtype=act, device=dev),
+            "dP": torch.empty((R, H), dtype=act, device=dev),
+            "dgamma": torch.empty(H, dtype=torch.float32, device=dev),
+            "dbeta": torch.empty(H, dtype=torch.float32, device=dev) if desc.norm == SP_LAYERNORM else None,
+        }
+        _check(sp_region_bwd(desc, dY, h, mask, mean, rstd, gamma, dR, out["d_res"], out["dP"],
+                             out["dgamma"], out["dbeta"], workspace,
+                             workspace.numel() * workspace.element_size(), s))
     return out
 
 
