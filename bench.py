@@ -47,6 +47,7 @@ SECONDARY = [("minimind_T2_S2048_B2_H768", 0), ("large_hidden_T8_S8192_B2_H8192"
              ("long_seq_T8_S32768_B1_H8192", 0), (DEFAULT_WORKLOAD, 1),
              ("large_hidden_T8_S8192_B2_H8192", 1)]
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
+CPU_SHARE = 16  # host cores one GPU's work may use on a shared host
 ROTATE_BYTES = 1.5e9
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -302,6 +303,32 @@ def measure(sp, w, shards, K, Wm, stream, flags=0, paired=False):
     return out, src, sets
 
 
+def roofline_entries(head, traffic):
+    """Roofline of the forward (the dominant kernel) and of the backward (its
+    main kernel plus the dgamma finish kernel where that schedule runs):
+    algorithmic bytes per launch over the launch duration measured with HIP
+    events on the kernels' stream; traffic = FETCH_SIZE + WRITE_SIZE per launch
+    from the committed counter summary of the same kernel source, else null."""
+    out = []
+    for direction, nbytes, us in (("fwd", head["fwd_bytes"], head["fwd_us_avg"]),
+                                  ("bwd", head["bwd_bytes"], head["bwd_us_avg"])):
+        achieved = nbytes / (us * 1e-6) / 1e9
+        t = None
+        if traffic is not None:
+            if direction == "fwd":
+                t = traffic["fwd_bytes_per_launch"]
+            else:
+                t = (traffic["bwd_main_fetch_bytes"] + traffic["bwd_main_write_bytes"] +
+                     traffic["bwd_finish_fetch_bytes"] + traffic["bwd_finish_write_bytes"])
+        out.append({"kernel": "sp_fwd_kernel" if direction == "fwd" else
+                    "sp_bwd_kernel (+ sp_dgamma_finish_kernel where it runs)",
+                    "direction": direction, "bound": "hbm", "algorithmic_bytes": nbytes,
+                    "launch_us": round(us, 3), "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": t,
+                    "traffic_over_algorithmic": None if t is None else round(t / nbytes, 3)})
+    return out
+
+
 def copy_reference(stream):
     import torch
     a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -377,8 +404,10 @@ def cpu_baseline(sp, w, j, src, outs, seconds):
                   within(outs.rstd[:n].cpu().numpy(), o["rstd"], 1e-5)])
     # the same oracle calls on disjoint row blocks from a thread pool (the C
     # oracle runs without the interpreter lock), on the host cores this process
-    # may use, at most 16
-    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    # may use, at most 16: one GPU's share of the host's cores, which the
+    # affinity mask of a shared host may not reflect
+    affinity = len(os.sched_getaffinity(0))
+    threads = max(1, min(CPU_SHARE, affinity))
     nt = int(max(1, min(w.R, probe * seconds * threads / t_probe / 2)))
     blocks = [(r0, min(nt, r0 + max(1, math.ceil(nt / threads))))
               for r0 in range(0, nt, max(1, math.ceil(nt / threads)))]
@@ -406,6 +435,9 @@ def cpu_baseline(sp, w, j, src, outs, seconds):
         "value": round(threaded_bytes / tt / 1e9, 4),
         "unit": "GB/s",
         "cores": threads,
+        "cores_in_affinity_mask": affinity,
+        "cores_note": f"threads = min({CPU_SHARE}, cores in the affinity mask): {CPU_SHARE} host cores are one "
+                      "GPU's share of a shared host",
         "kind": "oracle",
         "single_thread_value": round(sample_bytes / t / 1e9, 4),
         "threaded_sample": f"rows 0..{nt - 1} of shard {j} in {len(blocks)} blocks on {threads} threads, "
@@ -479,8 +511,9 @@ def main():
     j = w.shards[0]
     head, src, sets = measure(sp, w, (j,), args.steps, args.warmup, stream)
     copy_gbs = copy_reference(stream)
-    achieved = head["fwd_bytes"] / (head["fwd_us_avg"] * 1e-6) / 1e9
     traffic = load_traffic(w.name)
+    kernels = roofline_entries(head, traffic)
+    fwd_k = kernels[0]
     line = {
         "metric": "achieved HBM GB/s (and % of peak) for SP-region fused fwd+bwd on one shard",
         "value": round(head["value_GBs"], 2),
@@ -503,7 +536,11 @@ def main():
         "bwd_bytes": head["bwd_bytes"],
         "buffer_sets": head["buffer_sets"],
         "timing": {"method": "hip graph replay, host clock",
+                   "value_basis": "host clock around exactly K steps, synchronize on both sides "
+                                  "(includes the graph launch and synchronize latency)",
                    "gpu_event_ms_per_step": round(head["gpu_event_ms_per_step"], 6),
+                   "gpu_event_GBs": round(head["bytes_per_step"] / (head["gpu_event_ms_per_step"] * 1e-3) / 1e9, 2),
+                   "gpu_event_basis": "HIP events recorded on the kernels' stream around the same K steps",
                    "fwd_us_avg": round(head["fwd_us_avg"], 3), "fwd_us_median": round(head["fwd_us_median"], 3),
                    "bwd_us_avg": round(head["bwd_us_avg"], 3), "bwd_us_median": round(head["bwd_us_median"], 3),
                    "event_launches_each": head["event_launches_each"],
@@ -514,13 +551,14 @@ def main():
                  "cache_resident": head["warm_cache_resident"],
                  "note": "one buffer set repeated; not an HBM figure when cache_resident"},
         "roofline": {
-            "kernel": "sp_fwd_kernel",
+            "kernel": fwd_k["kernel"],
             "bound": "hbm",
-            "achieved": round(achieved, 2),
+            "achieved": fwd_k["achieved"],
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
-            "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": None if traffic is None else traffic["fwd_bytes_per_launch"],
+            "frac": fwd_k["frac"],
+            "traffic": fwd_k["traffic"],
+            "kernels": kernels,
         },
         "cpu_baseline": None,
         "workloads": {},
