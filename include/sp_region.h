@@ -54,6 +54,7 @@ extern "C" {
 
 #define SP_MAX_T 64          /* largest number of partials */
 #define SP_MAX_H_BYTES 131072 /* largest row: H * element_size */
+#define SP_NOALLOC_SCRATCH_BYTES (32u << 20) /* scratch held by sp_region_bwd_noalloc, per GPU */
 
 /* activation element type */
 enum { SP_F32 = 0, SP_BF16 = 1 };
@@ -76,7 +77,8 @@ enum {
     SP_EPARAM = -4,      /* bad norm, p, eps */
     SP_EALIGN = -5,      /* pointer not 16-byte aligned */
     SP_EWORKSPACE = -6,  /* workspace missing or too small */
-    SP_EHIP = -7         /* the HIP runtime refused the launch */
+    SP_EHIP = -7,        /* the HIP runtime refused the launch */
+    SP_ESCRATCH = -8     /* sp_region_bwd_noalloc: the shape needs more than SP_NOALLOC_SCRATCH_BYTES */
 };
 
 typedef struct sp_desc {
@@ -180,6 +182,28 @@ int sp_region_bwd(const sp_desc_t* d, const void* dY, const void* h, const uint8
                   const void* dR,
                   void* d_residual, void* dP, float* dgamma, float* dbeta,
                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sp_region_bwd without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Arguments, outputs and results are those of
+ * sp_region_bwd (bit for bit); the scratch comes from a static device array of
+ * SP_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on until
+ * the process ends, looked up on the first call on each device (that call also
+ * clears its arrival counts, with a kernel on `stream`).  The call itself
+ * allocates nothing.
+ *
+ * Returns SP_ESCRATCH, before anything is enqueued, when the descriptor needs
+ * more than SP_NOALLOC_SCRATCH_BYTES (sp_region_bwd_workspace_size(d) says how
+ * much it needs); then use sp_region_bwd with a workspace of that size.
+ * Every call on a GPU shares that GPU's scratch, which keeps the last call's
+ * contents: calls that overlap in time on one GPU (other streams, other host
+ * threads) race on it and must be ordered by the caller.
+ */
+int sp_region_bwd_noalloc(const sp_desc_t* d, const void* dY, const void* h, const uint8_t* mask,
+                          const float* mean, const float* rstd, const float* gamma,
+                          const void* dR,
+                          void* d_residual, void* dP, float* dgamma, float* dbeta, void* stream);
 
 /* Bytes of workspace sp_region_bwd needs for this descriptor: 0 when it needs
  * none (then the workspace may be NULL) and on a bad descriptor.  Host only;

@@ -283,6 +283,24 @@ def test_backward_schedule_by_shape(lib, shape, schedule):
         assert bwd_call(d, workspace=None) == -6
 
 
+def test_noalloc_rejects_shapes_beyond_its_scratch(lib):
+    """sp_region_bwd_noalloc refuses a shape whose backward needs more scratch
+    than the library holds, before any HIP call; descriptor errors come first."""
+    m = re.search(r"#define SP_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == sp.SP_NOALLOC_SCRATCH_BYTES
+    d = sp.make_desc(4096, 1, 16384, 2, 1, "bf16", "ln")  # 2048 rows of 16384: 33.6 MB of partial rows
+    assert sp.sp_region_bwd_workspace_size(d) > sp.SP_NOALLOC_SCRATCH_BYTES
+
+    def call(desc):
+        return sp.sp_region_bwd_noalloc(desc, fake(1), fake(2), fake(3), fake(4), fake(5), fake(6), None,
+                                        fake(7), fake(8), fake(9), fake(10), stream=0)
+
+    assert call(d) == -8
+    assert "SP_NOALLOC_SCRATCH_BYTES" in sp.sp_region_strerror(-8)
+    assert call(good_desc(S=66)) == -2
+    assert call(good_desc(p=1.0)) == -4
+
+
 def test_schedule_of_a_bad_descriptor(lib):
     assert lib.sp_region_bwd_schedule(None) == -1
     assert sp.sp_region_bwd_schedule(good_desc(S=66)) == -2

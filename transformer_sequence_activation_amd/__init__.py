@@ -3,8 +3,9 @@
 Argument marshalling only: every step of the forward and backward runs in the
 HIP kernels of csrc/sp_region.hip.  PyTorch supplies device memory and the
 stream.  The C entry points are exposed under their C names
-(`sp_region_fwd`, `sp_region_bwd`, `sp_region_bwd_workspace_size`,
-`sp_region_traffic_bytes`, `sp_region_strerror`, `sp_region_version`); `forward`
+(`sp_region_fwd`, `sp_region_bwd`, `sp_region_bwd_noalloc`,
+`sp_region_bwd_workspace_size`, `sp_region_bwd_schedule`, `sp_region_traffic_bytes`,
+`sp_region_strerror`, `sp_region_version`); `forward`
 and `backward` allocate the outputs with torch and call them.
 
 If the shared library is missing, `load()` raises: there is no fallback path.
@@ -20,9 +21,10 @@ SP_F32, SP_BF16 = 0, 1
 SP_RMSNORM, SP_LAYERNORM = 0, 1
 SP_FLAG_RECOMPUTE_MASK = 1
 SP_OK = 0
+SP_NOALLOC_SCRATCH_BYTES = 32 << 20
 STATUS = {0: "SP_OK", -1: "SP_EINVAL", -2: "SP_ESHAPE", -3: "SP_EDTYPE", -4: "SP_EPARAM",
-          -5: "SP_EALIGN", -6: "SP_EWORKSPACE", -7: "SP_EHIP"}
-EXPORTED = ("sp_region_fwd", "sp_region_bwd", "sp_region_bwd_workspace_size",
+          -5: "SP_EALIGN", -6: "SP_EWORKSPACE", -7: "SP_EHIP", -8: "SP_ESCRATCH"}
+EXPORTED = ("sp_region_fwd", "sp_region_bwd", "sp_region_bwd_noalloc", "sp_region_bwd_workspace_size",
             "sp_region_bwd_schedule", "sp_region_traffic_bytes", "sp_region_strerror",
             "sp_region_version")
 
@@ -67,6 +69,8 @@ def load(path=LIB_PATH):
     L.sp_region_fwd.restype = ctypes.c_int
     L.sp_region_bwd.argtypes = [pdesc, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.sp_region_bwd.restype = ctypes.c_int
+    L.sp_region_bwd_noalloc.argtypes = [pdesc, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.sp_region_bwd_noalloc.restype = ctypes.c_int
     L.sp_region_bwd_workspace_size.argtypes = [pdesc]
     L.sp_region_bwd_workspace_size.restype = sz
     L.sp_region_bwd_schedule.argtypes = [pdesc]
@@ -156,6 +160,14 @@ def sp_region_bwd(desc, dY, h, mask, mean, rstd, gamma, dR, d_residual, dP, dgam
                                 _ptr(rstd), _ptr(gamma), _ptr(dR), _ptr(d_residual), _ptr(dP),
                                 _ptr(dgamma), _ptr(dbeta), _ptr(workspace), workspace_bytes,
                                 _stream(stream))
+
+
+def sp_region_bwd_noalloc(desc, dY, h, mask, mean, rstd, gamma, dR, d_residual, dP, dgamma, dbeta,
+                          stream=None):
+    """Returns the status code (0 = success); see include/sp_region.h."""
+    return load().sp_region_bwd_noalloc(ctypes.byref(desc), _ptr(dY), _ptr(h), _ptr(mask), _ptr(mean),
+                                        _ptr(rstd), _ptr(gamma), _ptr(dR), _ptr(d_residual), _ptr(dP),
+                                        _ptr(dgamma), _ptr(dbeta), _stream(stream))
 
 
 # ---- convenience wrappers: allocate outputs with torch, raise on error ----

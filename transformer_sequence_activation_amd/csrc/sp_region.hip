@@ -35,6 +35,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "sp_region.h"
 
 #ifndef SP_BWD_TARGET_BLOCKS
@@ -1171,6 +1174,13 @@ __global__ __launch_bounds__(kFinGroups* kFinSlices) void sp_dgamma_finish_kerne
     }
 }
 
+// Zero n words (the arrival counts of a workspace that starts in an unknown
+// state); a kernel rather than a memset, so that it can sit in a captured graph.
+__global__ __launch_bounds__(256) void sp_clear_counts_kernel(uint32_t* p, int32_t n) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
 // ---------------------------------------------------------------------------
 // Launch layouts: (lanes per row, chunks per lane) by row length in chunks.
 
@@ -1494,6 +1504,7 @@ extern "C" const char* sp_region_strerror(int status) {
         case SP_EALIGN: return "tensor pointer not 16-byte aligned";
         case SP_EWORKSPACE: return "workspace missing or smaller than sp_region_bwd_workspace_size";
         case SP_EHIP: return g_hip_error;
+        case SP_ESCRATCH: return "the shape needs more backward scratch than SP_NOALLOC_SCRATCH_BYTES";
         default: return "unknown status";
     }
 }
@@ -1608,10 +1619,13 @@ extern "C" int sp_region_fwd(const sp_desc_t* d, const void* const* P, const voi
     return launch((const void*)k, (unsigned)grid, (unsigned)block, 0, stream, args);
 }
 
-extern "C" int sp_region_bwd(const sp_desc_t* d, const void* dY, const void* h, const uint8_t* mask,
-                             const float* mean, const float* rstd, const float* gamma, const void* dR,
-                             void* d_residual, void* dP, float* dgamma, float* dbeta, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+namespace {
+
+// The backward on a given workspace.  clear_counts: zero the workspace's
+// arrival counts (a small fill kernel on the same stream) before the backward.
+int bwd_enqueue(const sp_desc_t* d, const void* dY, const void* h, const uint8_t* mask, const float* mean,
+                const float* rstd, const float* gamma, const void* dR, void* d_residual, void* dP, float* dgamma,
+                float* dbeta, void* workspace, size_t workspace_bytes, void* stream, bool clear_counts) {
     int rc = check_desc(d);
     if (rc != SP_OK) return rc;
     const bool ln = d->norm == SP_LAYERNORM;
@@ -1685,6 +1699,13 @@ extern "C" int sp_region_bwd(const sp_desc_t* d, const void* dY, const void* h, 
 
     if (plan.variant < 0) return SP_ESHAPE;
     if (plan.blocks + plan.col_blocks > INT32_MAX) return SP_ESHAPE;
+    if (clear_counts) {
+        uint32_t* counts = (uint32_t*)workspace;
+        int32_t n = (int32_t)(kWsCountBytes / sizeof(uint32_t));
+        void* args[] = {&counts, &n};
+        rc = launch((const void*)sp_clear_counts_kernel, (unsigned)((n + 255) / 256), 256u, 0, stream, args);
+        if (rc != SP_OK) return rc;
+    }
     if (plan.blocks > 0) {
         const BwdKernel k = kBwd[d->dtype == SP_BF16 ? 1 : 0][d->norm == SP_LAYERNORM ? 1 : 0][dR ? 1 : 0]
                                 [regen ? 1 : 0][plan.col_blocks > 0 ? 1 : 0][plan.variant];
@@ -1702,4 +1723,64 @@ extern "C" int sp_region_bwd(const sp_desc_t* d, const void* dY, const void* h, 
     void* args[] = {&fin_ws, &fin_g, &fin_h, &fin_nacc, &dgamma, &dbeta};
     return launch((const void*)sp_dgamma_finish_kernel, fin_grid, (unsigned)(kFinGroups * kFinSlices), 0, stream,
                   args);
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of the backward entry point that allocates nothing: a device array
+// of SP_NOALLOC_SCRATCH_BYTES, one copy per GPU, alive until the process ends.
+// Host code never uses its name as an address: the address of each device's
+// copy is looked up once, with that device current, and kept.
+static __device__ __align__(256) uint8_t scratch[SP_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+    std::once_flag looked_up;
+    void* ptr = nullptr;
+    hipError_t err = hipSuccess;
+    std::atomic<bool> counts_cleared{false};
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+int scratch_of_current_device(ScratchSlot** slot) {
+    int dev = 0;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return record_hip(e);
+    if (dev < 0 || dev >= kMaxDevices) {
+        snprintf(g_hip_error, sizeof(g_hip_error), "device %d is past the %d devices the scratch serves", dev,
+                 kMaxDevices);
+        return SP_EHIP;
+    }
+    ScratchSlot& s = g_scratch[dev];
+    std::call_once(s.looked_up, [&s] { s.err = hipGetSymbolAddress(&s.ptr, HIP_SYMBOL(scratch)); });
+    if (s.err != hipSuccess) return record_hip(s.err);
+    *slot = &s;
+    return SP_OK;
+}
+
+}  // namespace
+
+extern "C" int sp_region_bwd(const sp_desc_t* d, const void* dY, const void* h, const uint8_t* mask,
+                             const float* mean, const float* rstd, const float* gamma, const void* dR,
+                             void* d_residual, void* dP, float* dgamma, float* dbeta, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    return bwd_enqueue(d, dY, h, mask, mean, rstd, gamma, dR, d_residual, dP, dgamma, dbeta, workspace,
+                       workspace_bytes, stream, false);
+}
+
+extern "C" int sp_region_bwd_noalloc(const sp_desc_t* d, const void* dY, const void* h, const uint8_t* mask,
+                                     const float* mean, const float* rstd, const float* gamma, const void* dR,
+                                     void* d_residual, void* dP, float* dgamma, float* dbeta, void* stream) {
+    const int rc = check_desc(d);
+    if (rc != SP_OK) return rc;
+    if (plan_bwd(d).ws_bytes > (size_t)SP_NOALLOC_SCRATCH_BYTES) return SP_ESCRATCH;
+    ScratchSlot* s = nullptr;
+    const int rs = scratch_of_current_device(&s);
+    if (rs != SP_OK) return rs;
+    // the arrival counts start at zero: cleared by this device's first call
+    // (they wrap back to zero at the end of every call after that)
+    const bool first = !s->counts_cleared.load();
+    const int rb = bwd_enqueue(d, dY, h, mask, mean, rstd, gamma, dR, d_residual, dP, dgamma, dbeta, s->ptr,
+                               (size_t)SP_NOALLOC_SCRATCH_BYTES, stream, first);
+    if (rb == SP_OK && first) s->counts_cleared.store(true);
+    return rb;
 }
