@@ -1,6 +1,6 @@
-"""Build the streaming-bandwidth probe (measure/stream_probe.hip) for gfx950.
+"""Build the measurement probes (measure/stream_probe.hip, measure/sync_probe.hip) for gfx950.
 
-    python -m measure.build        # writes measure/stream_probe
+    python -m measure.build        # writes measure/stream_probe and measure/sync_probe
 
 A measurement tool beside bench.py and profiles/, not part of the library.
 Like the library, the device code is compiled in a pass of its own with packed
@@ -10,17 +10,18 @@ import os
 import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SRC = os.path.join(HERE, "stream_probe.hip")
-PROBE = os.path.join(HERE, "stream_probe")
+PROBES = ("stream_probe", "sync_probe")
 
 
-def build(out=PROBE, verbose=True):
+def build(name, verbose=True):
+    src = os.path.join(HERE, name + ".hip")
+    out = os.path.join(HERE, name)
     hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
     common = [hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17"]
     fatbin, tmp = out + ".hipfb.tmp", out + ".tmp"
     cmds = [common + ["--cuda-device-only", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-                      SRC, "-o", fatbin],
-            common + ["--cuda-host-only", "-Xclang", "-fcuda-include-gpubinary", "-Xclang", fatbin, SRC,
+                      src, "-o", fatbin],
+            common + ["--cuda-host-only", "-Xclang", "-fcuda-include-gpubinary", "-Xclang", fatbin, src,
                       "-o", tmp]]
     try:
         for cmd in cmds:
@@ -36,4 +37,5 @@ def build(out=PROBE, verbose=True):
 
 
 if __name__ == "__main__":
-    print(build())
+    for name in PROBES:
+        print(build(name))

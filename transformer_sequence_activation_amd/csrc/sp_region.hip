@@ -109,6 +109,9 @@ struct Act<SP_F32> {
 #ifndef SP_EARLY_FLAGS
 #define SP_EARLY_FLAGS 1  // forward with T <= 2: keep flags made while the loads are in flight
 #endif
+#ifndef SP_EARLY_FLAGS_MAX_T
+#define SP_EARLY_FLAGS_MAX_T 2  // the largest fixed T whose forward makes its flags early
+#endif
 #ifndef SP_BWD_EARLY_FLAGS
 #define SP_BWD_EARLY_FLAGS 1  // mask-free backward, 2+ rows in flight: the same for its flags
 #endif
@@ -492,7 +495,7 @@ __global__ __launch_bounds__(BLOCK) void sp_fwd_kernel(const FwdArgs a) {
     float res[RPT][CPT][E];
     // With few partials the generator is a visible share of the work: its flags
     // (one bit per element) are then made while the loads are in flight.
-    constexpr bool kEarlyFlags = SP_EARLY_FLAGS && TT > 0 && TT <= 2;
+    constexpr bool kEarlyFlags = SP_EARLY_FLAGS && TT > 0 && TT <= SP_EARLY_FLAGS_MAX_T;
     uint32_t kbits[RPT][CPT];
     if constexpr (TT > 0) {
         u32x4 pv[RPT][CPT][TT];
