@@ -115,7 +115,7 @@ struct Timer {
         for (int w = 0; w < 3; ++w) launch(w);
         CHECK(hipDeviceSynchronize());
         CHECK(hipEventRecord(e0));
-        for (int k = 0; k < reps; ++k) launch(k);
+        for (int k = 0; k < reps; ++k) launch(k + 3);  // the warm-up sets are not reused
         CHECK(hipEventRecord(e1));
         CHECK(hipEventSynchronize(e1));
         CHECK(hipGetLastError());
@@ -132,7 +132,9 @@ constexpr int kReps = 60;
 
 static int rotations(int64_t bytes) {
     int64_t r = CAP / bytes;
-    return (int)(r > 24 ? 24 : r);
+    // one set per launch where the buffers allow (3 warm-up + kReps timed): more than the
+    // 256 MB Infinity Cache is cycled between two uses of a set
+    return (int)(r > kReps + 3 ? kReps + 3 : r);
 }
 
 template <int T, int CPL, int BLOCK, bool NTL, bool NTS>
