@@ -544,7 +544,7 @@ def main():
         "buffer_sets": head["buffer_sets"],
         "timing": {"method": "direct launches on one stream, host clock",
                    "value_basis": "host clock around exactly K steps, synchronize on both sides "
-                                  "(includes the graph launch and synchronize latency)",
+                                  "(includes the latency of the first launch and of the final synchronize)",
                    "gpu_event_ms_per_step": round(head["gpu_event_ms_per_step"], 6),
                    "gpu_event_GBs": round(head["bytes_per_step"] / (head["gpu_event_ms_per_step"] * 1e-3) / 1e9, 2),
                    "gpu_event_basis": "HIP events recorded on the kernels' stream around the same K steps",
