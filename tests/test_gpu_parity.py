@@ -657,6 +657,43 @@ def test_workspace_reused_across_calls_and_shapes():
     assert not bool(counts.any())  # every call left its arrival counts at zero
 
 
+def test_out_of_range_count_poisons_only_its_strip():
+    """A strip's arrival count above k - 1 (what a call that stopped part way can
+    leave) makes that strip's dgamma NaN and leaves every other output's bits
+    alone; the count then stays off zero, and a zero fill of the workspace
+    restores the normal bits.  The count is planted from the host: no kernel is
+    interrupted and nothing waits on it."""
+    print("\n[case] seg8 shard 0: planted out-of-range arrival count", flush=True)
+    w, j = SEG8_SHARD, 0
+    c = Case(w, "cuda")
+    f = gpu_fwd(c, j)
+    d = gdesc(w, j)
+    k = sp.sp_region_bwd_schedule(d)
+    assert k == 8
+    ref = gpu_bwd(c, j, f)
+    ws = torch.zeros(sp.sp_region_bwd_workspace_size(d), dtype=torch.uint8, device="cuda")
+    counts = ws[:4096].view(torch.int32)
+    strip, per_strip = 3, 8 * 8  # a strip is 8 chunks of 8 bf16 columns
+    counts[strip] = k + 5
+    args = (d, c.shard(c.dY, j), f["h"], f["mask"], f["mean"], f["rstd"], c.gamma)
+    got = sp.backward(*args, workspace=ws)
+    torch.cuda.synchronize()
+    poisoned = torch.zeros(w.H, dtype=torch.bool, device="cuda")
+    poisoned[strip * per_strip:(strip + 1) * per_strip] = True
+    assert bool(torch.isnan(got["dgamma"][poisoned]).all())
+    assert torch.equal(got["dgamma"][~poisoned], ref["dgamma"][~poisoned])
+    for key in ("d_res", "dP"):
+        assert torch.equal(got[key], ref[key]), key
+    left = counts.clone()
+    assert int(left[strip]) == k - 1 and not bool(left[:strip].any()) and not bool(left[strip + 1:].any())
+    ws.zero_()
+    again = sp.backward(*args, workspace=ws)
+    torch.cuda.synchronize()
+    for key in ("d_res", "dP", "dgamma"):
+        assert torch.equal(again[key], ref[key]), key
+    assert not bool(counts.any())
+
+
 @pytest.mark.parametrize("w,j", [(W.WORKLOADS["layernorm_T8_S4096_B1_H4096"], 3),
                                  (ROWS_SHARD, 1), (SEG8_SHARD, 1)],
                          ids=lambda v: getattr(v, "name", str(v)))
