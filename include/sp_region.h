@@ -36,9 +36,10 @@
  *              reaches that point.
  *   Errors     Argument errors are returned synchronously, before anything is
  *              enqueued.  A failed launch returns SP_EHIP (the text is kept for
- *              sp_region_strerror).  Calls are thread-safe and the library
- *              keeps no state of its own; the backward's workspace carries
- *              arrival counts from call to call (see sp_region_bwd).
+ *              sp_region_strerror).  Calls are thread-safe.  The library keeps
+ *              no state of its own apart from the per-GPU scratch array of
+ *              sp_region_bwd_noalloc; the backward's workspace carries arrival
+ *              counts from call to call (see sp_region_bwd).
  *   Empty      S == 0 or B == 0 is an empty shard: the forward enqueues
  *              nothing, the backward writes zeros to dgamma/dbeta.
  */
