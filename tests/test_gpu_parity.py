@@ -669,7 +669,10 @@ def test_out_of_range_count_poisons_only_its_strip():
     f = gpu_fwd(c, j)
     d = gdesc(w, j)
     k = sp.sp_region_bwd_schedule(d)
-    assert k == 8
+    if default_planner():
+        assert k == 8
+    elif k < 2:
+        pytest.skip("a build that forces partial rows keeps no arrival counts")
     ref = gpu_bwd(c, j, f)
     ws = torch.zeros(sp.sp_region_bwd_workspace_size(d), dtype=torch.uint8, device="cuda")
     counts = ws[:4096].view(torch.int32)
