@@ -390,6 +390,8 @@ EDGE = [
     (2, 6, 1, 65536, "bf16", "rms", 0.1, 1),    # the longest bf16 row
     (2, 4, 1, 32768, "f32", "ln", 0.1, 0),      # the longest fp32 row
     (4, 4096, 4, 128, "bf16", "ln", 0.1, 2),    # many short rows
+    (2, 38, 1, 712, "bf16", "ln", 0.1, 1),      # 89 chunks: 96-lane rows, 7 idle lanes, 19 rows (last pair ragged)
+    (3, 33, 1, 384, "f32", "rms", 0.1, 2),      # fp32, 96 chunks, run-time T, 11 rows
     (4, 400, 3, 2056, "bf16", "ln", 0.1, 1),    # 257 chunks: one ragged chunk past 256
     (2, 200, 1, 8192, "bf16", "ln", 0.2, 1),    # 1024-chunk rows, 100 rows
     (8, 64, 1, 4096, "bf16", "ln", 0.1, 5),     # 8 rows

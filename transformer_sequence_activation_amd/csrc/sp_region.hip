@@ -235,6 +235,34 @@ __device__ __forceinline__ float lanes_sum(float v) {
 // wavefront to have read them before returning.
 template <int TPR, int BLOCK, int NV, bool REUSE = true>
 __device__ __forceinline__ void group_sum(float (&v)[NV]) {
+    if constexpr (TPR > kWave && TPR % kWave != 0) {
+        // Row groups of a multiple of 32 lanes that wavefronts do not tile (96):
+        // each aligned 32-lane group sums its lanes, then the groups of a row are
+        // added in order through LDS.
+        static_assert(TPR % 32 == 0, "row groups are whole 32-lane groups");
+        constexpr int NG = TPR / 32;
+        constexpr int RPW = BLOCK / TPR;
+        __shared__ float red[RPW * NG * NV];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) v[i] = lanes_sum<32>(v[i]);
+        const int tid = threadIdx.x;
+        const int rg = tid / TPR;
+        const int g = (tid % TPR) / 32;
+        if ((tid & 31) == 0) {
+#pragma unroll
+            for (int i = 0; i < NV; ++i) red[(rg * NG + g) * NV + i] = v[i];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            float t = red[(rg * NG) * NV + i];
+#pragma unroll
+            for (int q = 1; q < NG; ++q) t += red[(rg * NG + q) * NV + i];
+            v[i] = t;
+        }
+        if constexpr (REUSE) __syncthreads();
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < NV; ++i) v[i] = lanes_sum<TPR>(v[i]);
     if constexpr (TPR > kWave) {
@@ -1198,7 +1226,8 @@ struct Layout {
 // generated from this list.
 #define SP_LAYOUT_LIST(X, ...)                                                                  \
     X(16, 1, 16, __VA_ARGS__), X(32, 1, 32, __VA_ARGS__), X(64, 1, 64, __VA_ARGS__),            \
-        X(128, 1, 112, __VA_ARGS__), X(64, 2, 128, __VA_ARGS__), X(256, 1, 256, __VA_ARGS__),   \
+        X(128, 1, 88, __VA_ARGS__), X(96, 1, 96, __VA_ARGS__), X(128, 1, 112, __VA_ARGS__),     \
+        X(64, 2, 128, __VA_ARGS__), X(256, 1, 256, __VA_ARGS__),                                 \
         X(512, 1, 512, __VA_ARGS__), X(512, 2, 1024, __VA_ARGS__), X(512, 4, 2048, __VA_ARGS__), \
         X(1024, 4, 4096, __VA_ARGS__), X(1024, 8, 8192, __VA_ARGS__)
 #define SP_LAYOUT_STRUCT(TPR, CPT, LIMIT, ...) Layout{TPR, CPT, LIMIT}
@@ -1217,7 +1246,9 @@ static_assert(layouts_ok(), "each layout holds its rows; limits increase up to t
 #endif
 constexpr int kSubWaveBlock = SP_SUBWAVE_BLOCK;  // block size of the layouts whose rows fit in one wavefront
 
-constexpr int block_of(int tpr) { return tpr <= kWave ? kSubWaveBlock : tpr; }
+// Row groups larger than a wavefront take one row per workgroup, except the
+// 96-lane ones, which take two (three whole wavefronts).
+constexpr int block_of(int tpr) { return tpr <= kWave ? kSubWaveBlock : (tpr % kWave ? 2 * tpr : tpr); }
 
 // Compile-time overrides (layout indices) used when tuning; -1 = default choice.
 #ifndef SP_FWD_LAYOUT
